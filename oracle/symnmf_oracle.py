@@ -1,0 +1,456 @@
+"""Plain, slow, fp64 CPU oracle for the SymNMF clustering hot path.
+
+TEST INFRASTRUCTURE ONLY: imported by the tests, by the smoke check and by the
+CPU-baseline leg of the benchmark, never by the library. It shares no code with
+the HIP path. Every function follows the pages in the pages' order and notation,
+with numpy as its only helper (a matmul, an argsort, LAPACK's eigvalsh):
+
+* P1 = "GPU-Accelerated Clustering for Financial Instruments at Scale"
+  (sections "Factorization at scale", "Choosing the rank k", "Factorizing with
+  SymNMF", "Why this solver", "The metric").
+* P2 = "GPU-Accelerated SymNMF Clustering Scales to a Million Financial
+  Instruments" (the same post; the displayed diagonal AdaGrad update and the
+  AdaptGrow algorithm sketch).
+* P3 = the paper-card page "GEM-KMeans: Memory-Efficient and Accurate
+  Clustering on Massive Scale with GPU Optimization", second abstract (the
+  SymNMF study: absolute Pearson correlation and TPDM inputs, trace identity,
+  Block-SVRG AdaptGrow).
+
+Where the pages leave a step open, the function says which reading it takes.
+Pins (what each function is checked against, other than itself) live in
+``tests/test_oracle_*.py``. Functions whose constants the pages do not fix and
+that nothing outside this file can pin say "parity unpinned" below:
+
+* ``tpdm`` constants (loss sign, F = R/(T+1), the 5% tail, 1/m scaling):
+  parity unpinned for the constants; the structure is pinned by invariants.
+* ``fit_adaptgrow`` stagnation rule and phi seeding: parity unpinned (the
+  pages name ``stagnating()`` and the seeding but do not define them).
+"""
+from __future__ import annotations
+
+import math
+
+import numpy as np
+
+__all__ = [
+    "standardize", "abs_corr", "abs_corr_rows", "tpdm_angles", "tpdm",
+    "tpdm_rows", "splitmix64", "uniform24", "init_uniform", "init_scale_matched",
+    "default_lr", "objective_explicit", "objective_trace", "gradient",
+    "adagrad_step", "fit_full", "sample_blocks", "svrg_sh_estimate",
+    "gap_ratio", "initial_blocks", "fit_adaptgrow", "top_eigenvalues",
+    "labels", "ari", "ari_pairs", "SOLVER_AUTO", "SOLVER_FULL",
+    "SOLVER_BLOCK_SVRG",
+]
+
+SOLVER_AUTO, SOLVER_FULL, SOLVER_BLOCK_SVRG = 0, 1, 2
+
+# --------------------------------------------------------------------------
+# Dependence matrices (P1 introduction: absolute Pearson correlation for
+# broad co-movement, TPDM for joint behaviour in extreme observations; P3).
+# --------------------------------------------------------------------------
+
+
+def standardize(X):
+    """Column-standardise a T x n returns window: z_ti = (x_ti - mu_i) / ||x_.i - mu_i||.
+
+    Unit-norm centred columns make Z^T Z the Pearson correlation matrix with no
+    ddof convention to choose. A constant column has no correlation; it raises.
+    """
+    X = np.asarray(X, dtype=np.float64)
+    mu = X.mean(axis=0)
+    C = X - mu
+    nrm = np.sqrt((C * C).sum(axis=0))
+    if np.any(nrm == 0):
+        raise ValueError("constant column: correlation undefined")
+    return C / nrm
+
+
+def abs_corr(X):
+    """S = |corr(X)|, n x n fp64 (P1 introduction: absolute Pearson correlation).
+
+    The diagonal is kept as computed (1 up to rounding)."""
+    Z = standardize(X)
+    return np.abs(Z.T @ Z)
+
+
+def abs_corr_rows(X, rows):
+    """Rows ``rows`` of |corr(X)| without forming the n x n matrix."""
+    Z = standardize(X)
+    rows = np.asarray(rows)
+    return np.abs(Z[:, rows].T @ Z)
+
+
+def tpdm_angles(X, tail_frac=0.05):
+    """The extreme-day angular components behind the TPDM.
+
+    Reading (parity unpinned for the constants; P1 introduction and P3 name
+    the TPDM from extreme value theory but print no recipe):
+      losses L = -X;  R_ti = ordinal rank of L_ti within column i (1..T,
+      ties to the earlier day);  F = R / (T + 1);  Frechet margins with
+      alpha = 2:  x_ti = (-1 / ln F_ti)^(1/2);  radius r_t = ||x_t.||_2;
+      the m = ceil(tail_frac * T) days of largest radius (ties to the
+      earlier day);  theta_t = x_t. / r_t.
+    Returns (theta m x n, selected days in radius order, m).
+    """
+    L = -np.asarray(X, dtype=np.float64)
+    T, n = L.shape
+    order = np.argsort(L, axis=0, kind="stable")
+    R = np.empty((T, n), dtype=np.int64)
+    np.put_along_axis(R, order, np.repeat(np.arange(1, T + 1)[:, None], n, axis=1), axis=0)
+    F = R / (T + 1.0)
+    xt = np.sqrt(-1.0 / np.log(F))
+    r = np.sqrt((xt * xt).sum(axis=1))
+    m = int(math.ceil(tail_frac * T - 1e-12))
+    m = max(1, min(T, m))
+    days = np.argsort(-r, kind="stable")[:m]
+    theta = xt[days] / r[days, None]
+    return theta, days, m
+
+
+def tpdm(X, tail_frac=0.05):
+    """S_ij = (1/m) sum over the m extreme days of theta_ti * theta_tj (n x n fp64)."""
+    theta, _, m = tpdm_angles(X, tail_frac)
+    return theta.T @ theta / m
+
+
+def tpdm_rows(X, rows, tail_frac=0.05):
+    theta, _, m = tpdm_angles(X, tail_frac)
+    rows = np.asarray(rows)
+    return theta[:, rows].T @ theta / m
+
+
+# --------------------------------------------------------------------------
+# Counter-based generator: SplitMix64 (Steele, Lea and Flood, "Fast splittable
+# pseudorandom number generators", OOPSLA 2014), written from its published
+# definition. Stream ``key``, counter c -> the (c+1)-th output of the
+# SplitMix64 sequence whose state starts at ``key``.
+# --------------------------------------------------------------------------
+
+_GOLDEN = np.uint64(0x9E3779B97F4A7C15)
+_M1 = np.uint64(0xBF58476D1CE4E5B9)
+_M2 = np.uint64(0x94D049BB133111EB)
+SAMPLER_KEY_XOR = 0x5851F42D4C957F2D
+
+
+def splitmix64(key, counter):
+    """Vectorised SplitMix64 output for state key + (counter + 1) * golden gamma."""
+    with np.errstate(over="ignore"):
+        z = np.uint64(key) + (np.asarray(counter, dtype=np.uint64) + np.uint64(1)) * _GOLDEN
+        z = (z ^ (z >> np.uint64(30))) * _M1
+        z = (z ^ (z >> np.uint64(27))) * _M2
+        return z ^ (z >> np.uint64(31))
+
+
+def uniform24(key, counter):
+    """Uniform on [0, 1): the top 24 bits of the SplitMix64 output times 2^-24."""
+    return (splitmix64(key, counter) >> np.uint64(40)).astype(np.float64) * 2.0 ** -24
+
+
+# --------------------------------------------------------------------------
+# Initialisation (P1 "Factorizing with SymNMF": the same fixed-seed
+# initialisation for every window, no warm start; P2 sketch: a scale-matched
+# init).
+# --------------------------------------------------------------------------
+
+
+def init_uniform(n, k, scale, seed):
+    """H0[i, c] = scale * u(seed, i*k + c)."""
+    idx = np.arange(n * k, dtype=np.uint64)
+    return (scale * uniform24(seed, idx)).reshape(n, k)
+
+
+def init_scale_matched(S_mean, k):
+    """Reading of the undefined scale-matched init: U(0, a) with
+    a = 2 sqrt(mean(S)/k), so E[(H0 H0^T)_ij] = k (a/2)^2 = mean(S)."""
+    return 2.0 * math.sqrt(S_mean / k)
+
+
+def default_lr(S_mean, k):
+    """Reading of the unspecified learning rate: eta = sqrt(mean(S)/k), the
+    mean entry of the scale-matched H0."""
+    return math.sqrt(S_mean / k)
+
+
+# --------------------------------------------------------------------------
+# Objective and gradient (P1 "Factorization at scale": the trace formulation
+# avoids n x n intermediates; P2 sketch: g = 4 (H (H^T H) - S H)).
+# --------------------------------------------------------------------------
+
+
+def objective_explicit(S, H):
+    """f(H) = ||S - H H^T||_F^2, the plain definition (forms n x n)."""
+    R = np.asarray(S, dtype=np.float64) - H @ H.T
+    return float((R * R).sum())
+
+
+def objective_trace(S_fro2, H, P):
+    """f = ||S||^2 - 2 tr(H^T S H) + ||H^T H||^2, with P = S H given."""
+    K = H.T @ H
+    return float(S_fro2 - 2.0 * (H * P).sum() + (K * K).sum())
+
+
+def gradient(S, H):
+    """grad f = 4 (H (H^T H) - S H) for symmetric S."""
+    return 4.0 * (H @ (H.T @ H) - S @ H)
+
+
+def adagrad_step(H, G, g, lr, eps=1e-8):
+    """P2 displayed update, element-wise: G <- G + g*g, then
+    H <- max(H - lr * g / (sqrt(G) + eps), 0). eps sits outside the root."""
+    G = G + g * g
+    H = np.maximum(H - lr * g / (np.sqrt(G) + eps), 0.0)
+    return H, G
+
+
+# --------------------------------------------------------------------------
+# Full-batch projected AdaGrad (P1 "Factorizing with SymNMF"; P2 sketch).
+# --------------------------------------------------------------------------
+
+
+def fit_full(S, H0, lr, max_iters, tol=0.0, eps=1e-8, G0=None, objective="trace"):
+    """Full-batch projected AdaGrad.
+
+    Iteration t: P = S H_t; f_t = f(H_t) (before the update); if t >= 1 and
+    |f_{t-1} - f_t| < tol * |f_{t-1}|, stop and return H_t; otherwise take the
+    AdaGrad step. At most ``max_iters`` steps.
+    Returns dict(H, G, f (list of f_t), iters (steps taken), converged).
+    """
+    S = np.asarray(S, dtype=np.float64)
+    H = np.array(H0, dtype=np.float64)
+    G = np.zeros_like(H) if G0 is None else np.array(G0, dtype=np.float64)
+    s2 = float((S * S).sum())
+    fs = []
+    converged = False
+    t = 0
+    while t < max_iters:
+        P = S @ H
+        f = objective_trace(s2, H, P) if objective == "trace" else objective_explicit(S, H)
+        fs.append(f)
+        if tol > 0 and t >= 1 and abs(fs[-2] - f) < tol * abs(fs[-2]):
+            converged = True
+            break
+        g = 4.0 * (H @ (H.T @ H) - P)
+        H, G = adagrad_step(H, G, g, lr, eps)
+        t += 1
+    return dict(H=H, G=G, f=fs, iters=t, converged=converged)
+
+
+# --------------------------------------------------------------------------
+# Block-SVRG AdaptGrow (P1 "Factorizing with SymNMF" and "Why this solver";
+# P2 sketch; P3 abstract).
+# --------------------------------------------------------------------------
+
+
+def sample_blocks(seed, t, nb, nsel):
+    """|B| = nsel distinct row blocks out of nb for step t, ascending.
+
+    Partial Fisher-Yates over [0, nb): for j < nsel, swap slot j with slot
+    j + (r_j mod (nb - j)), r_j = SplitMix64(seed ^ SAMPLER_KEY_XOR,
+    t * 2^32 + j)."""
+    key = np.uint64((int(seed) ^ SAMPLER_KEY_XOR) & 0xFFFFFFFFFFFFFFFF)
+    perm = list(range(nb))
+    for j in range(nsel):
+        r = int(splitmix64(key, np.uint64((t << 32) + j)))
+        pick = j + r % (nb - j)
+        perm[j], perm[pick] = perm[pick], perm[j]
+    return sorted(perm[:nsel])
+
+
+def svrg_sh_estimate(S, H, H_anchor, P_anchor, blocks, block_rows):
+    """Reading of block_svrg_grad's S H estimate: SVRG over row blocks.
+
+    C = sum over rows i of the sampled blocks of S[i, :]^T (H - H~)[i, :];
+    P_est = P~ + (nb / |B|) C. Unbiased since each block is drawn with
+    probability |B|/nb and S = S^T; H (H^T H) stays exact."""
+    n = S.shape[0]
+    nb = -(-n // block_rows)
+    rows = np.concatenate([np.arange(b * block_rows, min(n, (b + 1) * block_rows)) for b in blocks])
+    D = H[rows] - H_anchor[rows]
+    C = S[rows].T @ D
+    return P_anchor + (nb / len(blocks)) * C
+
+
+def gap_ratio(eigvals, k, floor_rel=1e-6):
+    """P1 "Why this solver": gamma_{k+1} = lambda_{k+1} / |lambda_{k+2}|,
+    eigenvalues 1-based in descending |lambda| with the sign kept. Reading: if
+    |lambda_{k+2}| <= floor_rel |lambda_1| the denominator is floor_rel |lambda_1|."""
+    ev = np.asarray(eigvals, dtype=np.float64)
+    lam1 = abs(ev[0])
+    den = abs(ev[k + 1])
+    if den <= floor_rel * lam1:
+        den = floor_rel * lam1
+    return float(ev[k] / den)
+
+
+def initial_blocks(gamma, nb, threshold=5.0):
+    """Reading of the phi seeding: gamma >= threshold -> all nb blocks (full
+    gradient); else |B|0 = 2^floor(log2(max(1, (gamma/threshold) nb)))."""
+    if gamma >= threshold:
+        return nb
+    x = max(1.0, gamma / threshold * nb)
+    return min(nb, 1 << int(math.floor(math.log2(x))))
+
+
+def fit_adaptgrow(S, H0, lr, max_iters, *, solver=SOLVER_AUTO, eigvals=None, k=None,
+                  phi0=0.0, block_rows=1024, gap_threshold=5.0, tol=1e-6,
+                  stall_tol=1e-3, eps=1e-8, seed=0):
+    """AdaptGrow: full-batch AdaGrad or Block-SVRG with sample growth.
+
+    Branch choice: FULL -> full; otherwise |B|0 from phi0 > 0
+    (ceil(phi0 nb) clamped to [1, nb]) or from gamma_{k+1} (``initial_blocks``);
+    |B|0 = nb means full.
+    Sampled branch (reading; the stagnation rule is parity unpinned): epochs of
+    E = ceil(nb/|B|) steps. The first step of an epoch is an anchor: P = S H
+    exactly, f exact; if a previous anchor exists and
+    (f~prev - f) < stall_tol f~prev the sample doubles (capped at nb; at nb the
+    run continues as full batch, keeping G); the anchor becomes H~ = H,
+    P~ = P and the step uses the exact gradient. Other steps draw
+    ``sample_blocks(seed, t, nb, |B|)`` and use ``svrg_sh_estimate``.
+    f of a sampled step is not computed (NaN in the trace). The full branch
+    tests convergence as ``fit_full`` does, against the previous step's exact f.
+    """
+    S = np.asarray(S, dtype=np.float64)
+    H = np.array(H0, dtype=np.float64)
+    n, kk = H.shape
+    if k is None:
+        k = kk
+    G = np.zeros_like(H)
+    s2 = float((S * S).sum())
+    nb = -(-n // block_rows)
+    gamma = None
+    if solver == SOLVER_FULL:
+        nsel = nb
+    elif phi0 > 0:
+        nsel = min(nb, max(1, int(math.ceil(phi0 * nb - 1e-12))))
+    else:
+        if eigvals is None:
+            raise ValueError("AdaptGrow needs eigenvalues or phi0")
+        gamma = gap_ratio(eigvals, k)
+        nsel = initial_blocks(gamma, nb, gap_threshold)
+    full = nsel >= nb
+    start_branch = "full" if full else "sampled"
+    fs = []
+    history = []
+    converged = False
+    prev_exact = None  # f of the immediately preceding step, if exact
+    epoch_pos = 0
+    E = -(-nb // nsel)
+    f_anchor_prev = None
+    H_a = P_a = None
+    t = 0
+    while t < max_iters:
+        K = H.T @ H
+        if full:
+            P = S @ H
+            f = float(s2 - 2.0 * (H * P).sum() + (K * K).sum())
+            fs.append(f)
+            if tol > 0 and prev_exact is not None and abs(prev_exact - f) < tol * abs(prev_exact):
+                converged = True
+                break
+            prev_exact = f
+        elif epoch_pos == 0:
+            P = S @ H
+            f = float(s2 - 2.0 * (H * P).sum() + (K * K).sum())
+            fs.append(f)
+            if f_anchor_prev is not None and (f_anchor_prev - f) < stall_tol * f_anchor_prev:
+                nsel = min(2 * nsel, nb)
+                E = -(-nb // nsel)
+                history.append((t, nsel))
+                if nsel >= nb:
+                    full = True
+            prev_exact = f
+            f_anchor_prev = f
+            H_a, P_a = H.copy(), P.copy()
+            epoch_pos = 0 if full else 1
+        else:
+            blocks = sample_blocks(seed, t, nb, nsel)
+            P = svrg_sh_estimate(S, H, H_a, P_a, blocks, block_rows)
+            fs.append(float("nan"))
+            prev_exact = None
+            epoch_pos += 1
+            if epoch_pos >= E:
+                epoch_pos = 0
+        g = 4.0 * (H @ K - P)
+        H, G = adagrad_step(H, G, g, lr, eps)
+        t += 1
+    return dict(H=H, G=G, f=fs, iters=t, converged=converged, history=history,
+                gamma=gamma, start_branch=start_branch,
+                final_branch="full" if full else "sampled", nsel=nsel)
+
+
+# --------------------------------------------------------------------------
+# Spectral probe (P1 "Choosing the rank k" and "Why this solver"): the
+# leading eigenvalues by magnitude, sign kept.
+# --------------------------------------------------------------------------
+
+
+def top_eigenvalues(S, p):
+    """The p eigenvalues of symmetric S of largest |lambda|, in descending
+    |lambda| (LAPACK eigvalsh is the plain definition here)."""
+    w = np.linalg.eigvalsh(np.asarray(S, dtype=np.float64))
+    order = np.argsort(-np.abs(w), kind="stable")
+    return w[order[:p]]
+
+
+# --------------------------------------------------------------------------
+# Labels and the adjusted Rand index (P1 "Factorizing with SymNMF": argmax of
+# a row of H is the hard label; "The metric": ARI).
+# --------------------------------------------------------------------------
+
+
+def labels(H):
+    """Row argmax of H, lowest column index on ties (an all-zero row -> 0)."""
+    H = np.asarray(H)
+    return np.argmax(H, axis=1).astype(np.int32)
+
+
+def ari(a, b):
+    """Adjusted Rand index (Hubert and Arabie 1985) from the contingency table."""
+    a = np.asarray(a)
+    b = np.asarray(b)
+    n = a.size
+    _, ai = np.unique(a, return_inverse=True)
+    _, bi = np.unique(b, return_inverse=True)
+    M = np.zeros((ai.max() + 1, bi.max() + 1), dtype=np.float64)
+    np.add.at(M, (ai, bi), 1.0)
+
+    def c2(x):
+        return x * (x - 1) / 2.0
+
+    sij = c2(M).sum()
+    sa = c2(M.sum(axis=1)).sum()
+    sb = c2(M.sum(axis=0)).sum()
+    tot = c2(float(n))
+    expected = sa * sb / tot if tot > 0 else 0.0
+    mx = 0.5 * (sa + sb)
+    if mx == expected:
+        return 1.0
+    return float((sij - expected) / (mx - expected))
+
+
+def ari_pairs(a, b):
+    """The same index by brute force over all pairs (for pins on tiny n)."""
+    a = list(a)
+    b = list(b)
+    n = len(a)
+    n11 = n10 = n01 = n00 = 0
+    for i in range(n):
+        for j in range(i + 1, n):
+            sa = a[i] == a[j]
+            sb = b[i] == b[j]
+            if sa and sb:
+                n11 += 1
+            elif sa:
+                n10 += 1
+            elif sb:
+                n01 += 1
+            else:
+                n00 += 1
+    tot = n11 + n10 + n01 + n00
+    if tot == 0:
+        return 1.0
+    expected = (n11 + n10) * (n11 + n01) / tot
+    mx = 0.5 * ((n11 + n10) + (n11 + n01))
+    if mx == expected:
+        return 1.0
+    return (n11 - expected) / (mx - expected)

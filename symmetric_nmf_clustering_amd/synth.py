@@ -1,0 +1,164 @@
+"""Seeded synthetic return windows with planted groups.
+
+This module only draws inputs: a T x n window of daily returns X (day-major,
+float32) and the planted group label of every instrument. It holds none of the
+clustering method's arithmetic, so both the HIP path and the CPU oracle may take
+their inputs from it.
+
+The pages ("GPU-Accelerated Clustering for Financial Instruments at Scale",
+sections "The temporal setup" and "Choosing the rank k") describe a synthetic
+return stream with planted groups of planted rank 24 and a joint tail-stress
+episode, but do not print the generator. The recipes below are the workload
+definitions this library is measured on:
+
+* ``gaussian_blocks``: n instruments in k equal groups, r = a*f_g + b*e with
+  f, e iid N(0, 1) (n=1024, k=8, T=256, a=0.6, b=0.8, seed 0).
+* ``student_factor``: k groups of size 64 + Multinomial(n - 64k, 1/k), group
+  membership by a seeded permutation, per-instrument loading l ~ U(0.3, 0.9),
+  r = l*f_g + sqrt(1 - l^2)*e with f and e Student-t (df 4) divided by sqrt(2)
+  so they have unit variance.
+* ``student_factor_stress``: the same, plus a joint crash: on 10 contiguous
+  days starting at a seeded day, every member of the first 4 groups of a
+  seeded group permutation receives an extra -5 (five unit standard
+  deviations).
+
+Draw order (numpy ``default_rng(seed)``) is fixed and documented per function,
+so a recipe is reproducible from its name, sizes and seed alone.
+"""
+from __future__ import annotations
+
+from dataclasses import dataclass, field
+
+import numpy as np
+
+
+@dataclass
+class Window:
+    """One synthetic window: returns X (T x n, float32, day-major) and labels."""
+
+    X: np.ndarray
+    labels: np.ndarray
+    k: int
+    recipe: str
+    seed: int
+    meta: dict = field(default_factory=dict)
+
+    @property
+    def T(self) -> int:
+        return self.X.shape[0]
+
+    @property
+    def n(self) -> int:
+        return self.X.shape[1]
+
+
+def _t4_unit(rng: np.random.Generator, shape) -> np.ndarray:
+    # Student-t with 4 degrees of freedom has variance 4/(4-2) = 2.
+    return rng.standard_t(4, size=shape) / np.sqrt(2.0)
+
+
+def gaussian_blocks(n: int = 1024, k: int = 8, T: int = 256, a: float = 0.6,
+                    b: float = 0.8, seed: int = 0) -> Window:
+    """Equal groups, Gaussian factors and noise.
+
+    Draw order: group permutation (n), factors F (T x k), noise E (T x n).
+    """
+    if n % k:
+        raise ValueError("gaussian_blocks needs n divisible by k")
+    rng = np.random.default_rng(seed)
+    perm = rng.permutation(n)
+    labels = np.empty(n, dtype=np.int32)
+    labels[perm] = np.repeat(np.arange(k, dtype=np.int32), n // k)
+    F = rng.standard_normal((T, k))
+    E = rng.standard_normal((T, n))
+    X = a * F[:, labels] + b * E
+    return Window(X.astype(np.float32), labels, k, "gaussian_blocks", seed,
+                  {"a": a, "b": b})
+
+
+def _student_groups(rng, n, k, min_size):
+    if n < min_size * k:
+        raise ValueError("n too small for k groups of the minimum size")
+    sizes = min_size + rng.multinomial(n - min_size * k, np.full(k, 1.0 / k))
+    perm = rng.permutation(n)
+    labels = np.empty(n, dtype=np.int32)
+    labels[perm] = np.repeat(np.arange(k, dtype=np.int32), sizes)
+    return sizes, labels
+
+
+def student_factor(n: int = 8192, k: int = 24, T: int = 252, seed: int = 1,
+                   min_size: int = 64) -> Window:
+    """Student-t planted-factor returns.
+
+    Draw order: group sizes (multinomial), membership permutation (n),
+    loadings l (n), factors F (T x k), noise E (T x n).
+    """
+    rng = np.random.default_rng(seed)
+    sizes, labels = _student_groups(rng, n, k, min_size)
+    load = rng.uniform(0.3, 0.9, size=n)
+    F = _t4_unit(rng, (T, k))
+    E = _t4_unit(rng, (T, n))
+    X = load * F[:, labels] + np.sqrt(1.0 - load * load) * E
+    return Window(X.astype(np.float32), labels, k, "student_factor", seed,
+                  {"sizes": sizes.tolist()})
+
+
+def student_factor_stress(n: int = 8192, k: int = 24, T: int = 252,
+                          seed: int = 1, min_size: int = 64,
+                          stress_groups: int = 4, stress_days: int = 10,
+                          shock: float = -5.0) -> Window:
+    """``student_factor`` plus a joint tail-stress episode.
+
+    The draws of ``student_factor`` come first (same seed gives the same
+    calm returns), then: a permutation of the k groups (the first
+    ``stress_groups`` are stressed) and the first stressed day, uniform on
+    [0, T - stress_days].
+    """
+    base = student_factor(n, k, T, seed, min_size)
+    rng = np.random.default_rng([seed, 1])
+    gperm = rng.permutation(k)
+    groups = np.sort(gperm[:stress_groups])
+    day0 = int(rng.integers(0, T - stress_days + 1))
+    X = base.X.astype(np.float64)
+    members = np.isin(base.labels, groups)
+    X[day0:day0 + stress_days, members] += shock
+    meta = dict(base.meta)
+    meta.update({"stress_groups": groups.tolist(), "stress_day0": day0,
+                 "stress_days": stress_days, "shock": shock})
+    return Window(X.astype(np.float32), base.labels, k,
+                  "student_factor_stress", seed, meta)
+
+
+# Named workloads: (recipe, kwargs).  The sizes are the ones the library is
+# measured and parity-tested on.
+WORKLOADS = {
+    "blocks_n1024_k8": (gaussian_blocks, dict(n=1024, k=8, T=256, seed=0)),
+    "tfactor_n8192_k24": (student_factor, dict(n=8192, k=24, T=252, seed=1)),
+    "tstress_n8192_k24": (student_factor_stress,
+                          dict(n=8192, k=24, T=252, seed=1)),
+    "tfactor_n100000_k24": (student_factor,
+                            dict(n=100000, k=24, T=252, seed=2)),
+}
+
+
+def workload(name: str, **overrides) -> Window:
+    fn, kw = WORKLOADS[name]
+    kw = dict(kw)
+    kw.update(overrides)
+    return fn(**kw)
+
+
+def random_symmetric_nonneg(n: int, seed: int, dtype=np.float32) -> np.ndarray:
+    """A seeded dense symmetric nonnegative matrix (uniform [0, 1) entries),
+    for kernel tests that need an S without a returns window."""
+    rng = np.random.default_rng(seed)
+    A = rng.random((n, n))
+    S = np.triu(A) + np.triu(A, 1).T
+    return S.astype(dtype)
+
+
+def random_factor(n: int, k: int, seed: int, scale: float = 1.0,
+                  dtype=np.float32) -> np.ndarray:
+    """A seeded nonnegative n x k factor, uniform on [0, scale)."""
+    rng = np.random.default_rng(seed)
+    return (scale * rng.random((n, k))).astype(dtype)

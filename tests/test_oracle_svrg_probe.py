@@ -1,0 +1,173 @@
+"""Pins for the oracle's generator, Block-SVRG estimator, gap rule, spectral
+truth, labels and ARI."""
+import itertools
+import os
+
+import numpy as np
+import pytest
+
+import oracle
+
+
+def test_splitmix64_known_answers(golden_dir):
+    with open(os.path.join(golden_dir, "splitmix64_seed0.txt")) as fh:
+        rows = [l.split() for l in fh if l.strip() and not l.startswith("#")]
+    for c, hexval in rows:
+        assert int(oracle.splitmix64(0, np.uint64(int(c)))) == int(hexval, 16)
+
+
+def test_splitmix64_is_the_sequence():
+    # counter c is output c+1 of the sequential generator with state `key`
+    key = 0x1234_5678_9ABC_DEF0
+    state = key
+    mask = (1 << 64) - 1
+    for c in range(5):
+        state = (state + 0x9E3779B97F4A7C15) & mask
+        z = state
+        z = ((z ^ (z >> 30)) * 0xBF58476D1CE4E5B9) & mask
+        z = ((z ^ (z >> 27)) * 0x94D049BB133111EB) & mask
+        z ^= z >> 31
+        assert int(oracle.splitmix64(key, np.uint64(c))) == z
+
+
+def test_uniform24_range_and_grid():
+    u = oracle.uniform24(7, np.arange(100000, dtype=np.uint64))
+    assert u.min() >= 0.0 and u.max() < 1.0
+    assert np.all(u * 2 ** 24 == np.floor(u * 2 ** 24))
+    assert abs(u.mean() - 0.5) < 0.005
+
+
+def test_init_layout():
+    H = oracle.init_uniform(3, 2, 0.1, 5)
+    flat = 0.1 * oracle.uniform24(5, np.arange(6, dtype=np.uint64))
+    np.testing.assert_array_equal(H.ravel(), flat)
+
+
+def test_sample_blocks_valid_and_uniform():
+    counts = np.zeros(10)
+    for t in range(4000):
+        b = oracle.sample_blocks(3, t, 10, 3)
+        assert b == sorted(set(b)) and len(b) == 3 and 0 <= b[0] and b[-1] < 10
+        counts[b] += 1
+    expect = 4000 * 3 / 10
+    assert np.abs(counts - expect).max() < 5 * np.sqrt(expect)
+    assert oracle.sample_blocks(3, 1, 10, 10) == list(range(10))
+
+
+def _sym(n, seed):
+    A = np.random.default_rng(seed).random((n, n))
+    return (A + A.T) / 2
+
+
+def test_svrg_full_sample_is_exact():
+    n, b = 37, 10
+    S = _sym(n, 1)
+    rng = np.random.default_rng(2)
+    H, Ha = rng.random((n, 3)), rng.random((n, 3))
+    est = oracle.svrg_sh_estimate(S, H, Ha, S @ Ha, list(range(4)), b)
+    np.testing.assert_allclose(est, S @ H, rtol=1e-13)
+
+
+def test_svrg_unbiased_by_enumeration():
+    # averaging the estimate over every |B| = 1 subset of nb = 4 blocks (unequal
+    # last block) gives exactly S H
+    n, b = 35, 10
+    S = _sym(n, 3)
+    rng = np.random.default_rng(4)
+    H, Ha = rng.random((n, 2)), rng.random((n, 2))
+    Pa = S @ Ha
+    for size in (1, 2, 3):
+        subsets = list(itertools.combinations(range(4), size))
+        mean = sum(oracle.svrg_sh_estimate(S, H, Ha, Pa, list(s), b) for s in subsets) / len(subsets)
+        np.testing.assert_allclose(mean, S @ H, rtol=1e-12)
+
+
+def test_gap_ratio_and_seeding():
+    ev = np.array([10.0, 9.0, 8.0, 1.0, -0.5, 0.1])
+    assert oracle.gap_ratio(ev, 2) == pytest.approx(8.0 / 1.0)
+    assert oracle.gap_ratio(ev, 3) == pytest.approx(1.0 / 0.5)
+    assert oracle.initial_blocks(8.0, 16) == 16              # clean gap -> full
+    assert oracle.initial_blocks(2.0, 16) == 4               # 2/5*16 = 6.4 -> 4
+    assert oracle.initial_blocks(0.01, 16) == 1
+    # floored denominator for an exactly low-rank spectrum
+    ev0 = np.array([1.0, 0.5, 1e-3, 0.0])
+    assert oracle.gap_ratio(ev0, 1) == pytest.approx(0.5 / 1e-3)
+    assert oracle.gap_ratio(ev0, 2) == pytest.approx(1e-3 / 1e-6)
+
+
+def test_adaptgrow_full_equals_fit_full():
+    S = _sym(50, 5)
+    H0 = oracle.init_uniform(50, 3, 0.4, 9)
+    a = oracle.fit_adaptgrow(S, H0, 0.03, 60, solver=oracle.SOLVER_FULL, tol=1e-5)
+    b = oracle.fit_full(S, H0, 0.03, 60, tol=1e-5)
+    np.testing.assert_array_equal(a["H"], b["H"])
+    assert a["f"] == b["f"] and a["iters"] == b["iters"]
+
+
+def test_adaptgrow_branch_choice():
+    # gamma_{k+1} = lambda_{k+1}/|lambda_{k+2}|: a common factor at k+1 with a
+    # clean drop after it selects the full branch
+    k, s = 3, 20
+    truth = np.repeat(np.arange(k), s)
+    S = 0.9 * (truth[:, None] == truth[None, :]) + 0.05
+    H0 = oracle.init_uniform(k * s, k, 0.3, 0)
+    clean = np.array([21.0, 18.0, 18.0, 6.0, 1.0])
+    out = oracle.fit_adaptgrow(S, H0, 0.05, 5, eigvals=clean, k=k, block_rows=8)
+    assert out["start_branch"] == "full" and out["gamma"] == pytest.approx(6.0)
+    # a flat post-rank spectrum starts sampled
+    flat = np.array([5.0, 4.0, 3.0, 1.0, 1.0, 1.0])
+    out = oracle.fit_adaptgrow(S, H0, 0.05, 5, eigvals=flat, k=3, block_rows=8)
+    assert out["start_branch"] == "sampled" and out["nsel"] < -(-60 // 8)
+    # the planted matrix itself has only k signal eigenvalues (its offset lies
+    # in the span of the group indicators), so gamma_{k+1} compares two zeros
+    ev = oracle.top_eigenvalues(S, k + 2)
+    assert oracle.gap_ratio(ev, k) < 5.0
+
+
+def test_adaptgrow_sampled_keeps_nonnegative_and_anchor_objectives_exact():
+    n, k = 48, 3
+    S = _sym(n, 6)
+    H0 = oracle.init_uniform(n, k, 0.3, 2)
+    out = oracle.fit_adaptgrow(S, H0, 0.01, 25, phi0=0.25, block_rows=8, tol=0.0, seed=4)
+    assert out["H"].min() >= 0
+    f = np.array(out["f"])
+    E = 6 // 2  # nb = 6, |B| = ceil(0.25*6) = 2
+    assert np.all(np.isfinite(f[::E])) and np.all(np.isnan(np.delete(f, np.arange(0, len(f), E))))
+
+
+def test_top_eigenvalues_planted_closed_form():
+    # (c - mu) blockdiag(1 1^T) + mu 1 1^T with k equal blocks of size s:
+    # eigenvalues (c-mu) s + mu n (once), (c-mu) s (k-1 times), then 0
+    k, s, c, mu = 4, 25, 0.8, 0.1
+    n = k * s
+    truth = np.repeat(np.arange(k), s)
+    S = (c - mu) * (truth[:, None] == truth[None, :]) + mu
+    ev = oracle.top_eigenvalues(S, k + 2)
+    np.testing.assert_allclose(ev[0], (c - mu) * s + mu * n, rtol=1e-12)
+    np.testing.assert_allclose(ev[1:k], (c - mu) * s, rtol=1e-12)
+    assert np.all(np.abs(ev[k:]) < 1e-10)
+
+
+def test_top_eigenvalues_magnitude_order_keeps_sign():
+    S = np.diag([1.0, -5.0, 3.0, -0.5])
+    np.testing.assert_array_equal(oracle.top_eigenvalues(S, 3), [-5.0, 3.0, 1.0])
+
+
+def test_labels_ties_and_zero_rows():
+    H = np.array([[0.0, 0.0, 0.0], [0.2, 0.5, 0.5], [0.7, 0.1, 0.7], [0.1, 0.2, 0.3]])
+    np.testing.assert_array_equal(oracle.labels(H), [0, 1, 0, 2])
+
+
+def test_ari_bruteforce_and_sklearn():
+    rng = np.random.default_rng(0)
+    for trial in range(30):
+        n = int(rng.integers(2, 13))
+        a = rng.integers(0, 4, n)
+        b = rng.integers(0, 3, n)
+        assert oracle.ari(a, b) == pytest.approx(oracle.ari_pairs(a, b), abs=1e-12)
+    sk = pytest.importorskip("sklearn.metrics")
+    for trial in range(10):
+        a = rng.integers(0, 6, 200)
+        b = np.where(rng.random(200) < 0.7, a, rng.integers(0, 6, 200))
+        assert oracle.ari(a, b) == pytest.approx(sk.adjusted_rand_score(a, b), abs=1e-12)
+    assert oracle.ari([0, 0, 1, 1], [5, 5, 2, 2]) == 1.0
