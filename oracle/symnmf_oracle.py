@@ -35,7 +35,7 @@ import numpy as np
 __all__ = [
     "standardize", "abs_corr", "abs_corr_rows", "tpdm_angles", "tpdm",
     "tpdm_rows", "splitmix64", "uniform24", "init_uniform", "init_scale_matched",
-    "default_lr", "objective_explicit", "objective_trace", "gradient",
+    "default_lr", "sh_product", "objective_explicit", "objective_trace", "gradient",
     "adagrad_step", "fit_full", "sample_blocks", "svrg_sh_estimate",
     "gap_ratio", "initial_blocks", "fit_adaptgrow", "top_eigenvalues",
     "labels", "ari", "ari_pairs", "SOLVER_AUTO", "SOLVER_FULL",
@@ -88,8 +88,9 @@ def tpdm_angles(X, tail_frac=0.05):
       losses L = -X;  R_ti = ordinal rank of L_ti within column i (1..T,
       ties to the earlier day);  F = R / (T + 1);  Frechet margins with
       alpha = 2:  x_ti = (-1 / ln F_ti)^(1/2);  radius r_t = ||x_t.||_2;
-      the m = ceil(tail_frac * T) days of largest radius (ties to the
-      earlier day);  theta_t = x_t. / r_t.
+      the m = ceil(tail_frac * T - 1e-4) days of largest radius (ties to the
+      earlier day; the slack keeps a tail fraction whose product with T is an
+      integer up to rounding at that integer);  theta_t = x_t. / r_t.
     Returns (theta m x n, selected days in radius order, m).
     """
     L = -np.asarray(X, dtype=np.float64)
@@ -100,7 +101,7 @@ def tpdm_angles(X, tail_frac=0.05):
     F = R / (T + 1.0)
     xt = np.sqrt(-1.0 / np.log(F))
     r = np.sqrt((xt * xt).sum(axis=1))
-    m = int(math.ceil(tail_frac * T - 1e-12))
+    m = int(math.ceil(tail_frac * T - 1e-4))
     m = max(1, min(T, m))
     days = np.argsort(-r, kind="stable")[:m]
     theta = xt[days] / r[days, None]
@@ -175,6 +176,13 @@ def default_lr(S_mean, k):
 # Objective and gradient (P1 "Factorization at scale": the trace formulation
 # avoids n x n intermediates; P2 sketch: g = 4 (H (H^T H) - S H)).
 # --------------------------------------------------------------------------
+
+
+def sh_product(S, H):
+    """P = S H and tr(H^T S H) = sum_i <H_i, P_i> (the product every full-batch
+    step needs; P1 "Factorization at scale")."""
+    P = np.asarray(S, dtype=np.float64) @ np.asarray(H, dtype=np.float64)
+    return P, float((np.asarray(H, dtype=np.float64) * P).sum())
 
 
 def objective_explicit(S, H):

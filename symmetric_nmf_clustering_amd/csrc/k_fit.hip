@@ -1,0 +1,424 @@
+// Fit kernels: S statistics, initialisation, the fused reduce + gradient +
+// projected AdaGrad + Gram kernel, the per-step finalisation, labels, and the
+// small dense helpers of the spectral probe.
+//
+// P1 "Factorizing with SymNMF" (diagonal AdaGrad, element-wise) and P2 (the
+// displayed update G <- G + g*g, H <- max(H - eta g/(sqrt(G) + eps), 0); the
+// AdaptGrow sketch's gradient 4 (H (H^T H) - S H)); P1 "Factorization at
+// scale" (objective by the trace identity, no n x n intermediates).
+#include <math.h>
+
+#include "common.h"
+#include "kernels.h"
+
+namespace symnmf {
+
+// ---- S statistics: per 64-row block, sum S and sum S^2 (fp64) ---------------
+__global__ __launch_bounds__(256) void s_stats_kernel(const float* __restrict__ S, int64_t lds,
+                                                      int n, double* __restrict__ part2) {
+    __shared__ double red[4];
+    const int row0 = blockIdx.x * 64;
+    const int rows = min(64, n - row0);
+    double s1 = 0.0, s2 = 0.0;
+    for (int rr = 0; rr < rows; ++rr) {
+        const float* row = S + (int64_t)(row0 + rr) * lds;
+        float a1 = 0.f, a2 = 0.f;  // <= n/256 terms per thread per row
+        for (int c = threadIdx.x; c < n; c += 256) {
+            const float v = row[c];
+            a1 += v;
+            a2 += v * v;
+        }
+        s1 += a1;
+        s2 += a2;
+    }
+    const double t1 = block_sum256(s1, red);
+    const double t2 = block_sum256(s2, red);
+    if (threadIdx.x == 0) {
+        part2[2 * blockIdx.x] = t1;
+        part2[2 * blockIdx.x + 1] = t2;
+    }
+}
+
+__global__ __launch_bounds__(256) void s_stats_final_kernel(const double* __restrict__ part2,
+                                                            int nblk, double* __restrict__ out2) {
+    __shared__ double red[4];
+    double a = 0.0, b = 0.0;
+    for (int i = threadIdx.x; i < nblk; i += 256) {
+        a += part2[2 * i];
+        b += part2[2 * i + 1];
+    }
+    a = block_sum256(a, red);
+    b = block_sum256(b, red);
+    if (threadIdx.x == 0) {
+        out2[0] = a;
+        out2[1] = b;
+    }
+}
+
+hipError_t launch_s_stats(const float* S, int64_t lds, int n, double* part2, hipStream_t st) {
+    const int nblk = (n + 63) / 64;
+    hipLaunchKernelGGL(s_stats_kernel, dim3(nblk), dim3(256), 0, st, S, lds, n, part2);
+    return hipGetLastError();
+}
+hipError_t launch_s_stats_final(const double* part2, int nblk, double* out2, hipStream_t st) {
+    hipLaunchKernelGGL(s_stats_final_kernel, dim3(1), dim3(256), 0, st, part2, nblk, out2);
+    return hipGetLastError();
+}
+
+// ---- element-wise helpers -------------------------------------------------------
+__global__ void init_uniform_kernel(float* __restrict__ H, int64_t count, float scale,
+                                    float shift, uint64_t seed) {
+    const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (i < count) H[i] = scale * uniform24(seed, (uint64_t)i) + shift;
+}
+hipError_t launch_init_uniform(float* H, int64_t count, float scale, float shift, uint64_t seed,
+                               hipStream_t st) {
+    if (count <= 0) return hipSuccess;
+    hipLaunchKernelGGL(init_uniform_kernel, dim3((unsigned)((count + 255) / 256)), dim3(256), 0,
+                       st, H, count, scale, shift, seed);
+    return hipGetLastError();
+}
+
+__global__ void fill_kernel(float* __restrict__ p, int64_t count, float v) {
+    const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (i < count) p[i] = v;
+}
+hipError_t launch_fill(float* p, int64_t count, float v, hipStream_t st) {
+    if (count <= 0) return hipSuccess;
+    hipLaunchKernelGGL(fill_kernel, dim3((unsigned)((count + 255) / 256)), dim3(256), 0, st, p,
+                       count, v);
+    return hipGetLastError();
+}
+
+__global__ void copy_kernel(float* __restrict__ d, const float* __restrict__ s, int64_t count) {
+    const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (i < count) d[i] = s[i];
+}
+hipError_t launch_copy(float* dst, const float* src, int64_t count, hipStream_t st) {
+    if (count <= 0) return hipSuccess;
+    hipLaunchKernelGGL(copy_kernel, dim3((unsigned)((count + 255) / 256)), dim3(256), 0, st, dst,
+                       src, count);
+    return hipGetLastError();
+}
+
+// ---- fused update ------------------------------------------------------------
+// One workgroup per kUpdRows rows. For each element (i, c):
+//   P   = sum_s part[s][i][c]            (exact pass, fixed split order)
+//      or P~[i][c] + pscale * sum_s ...  (Block-SVRG estimate)
+//   g   = 4 ((H K)[i][c] - P)
+//   G'  = G + g*g
+//   H'  = max(H - lr g / (sqrt(G') + eps), 0)
+// plus <H_t, P> per block (fp64) for the trace identity and the partial Gram
+// H'^T H' of the block's rows for the next step's K.
+__global__ __launch_bounds__(256) void update_kernel(UpdateArgs a) {
+    if (a.fd->done) return;
+    extern __shared__ float smem[];
+    const int k = a.k;
+    float* Hs = smem;                  // kUpdRows x k   H_t rows
+    float* Hn_s = Hs + kUpdRows * k;   // kUpdRows x k   H_{t+1} rows
+    float* Ks = Hn_s + kUpdRows * k;   // k x k
+    __shared__ double red[4];
+
+    const int row0 = blockIdx.x * kUpdRows;
+    const int rows = min(kUpdRows, a.n - row0);
+    const int nel = rows * k;
+    const int tid = threadIdx.x;
+
+    for (int e = tid; e < kUpdRows * k; e += 256) {
+        const int i = e / k;
+        Hs[e] = (i < rows) ? a.H[(int64_t)row0 * k + e] : 0.f;
+    }
+    if (!a.gram_only)
+        for (int e = tid; e < k * k; e += 256) Ks[e] = a.fd->K[(e / k) * kMaxK + (e % k)];
+    __syncthreads();
+
+    double tr = 0.0;
+    if (a.gram_only) {
+        for (int e = tid; e < kUpdRows * k; e += 256) Hn_s[e] = Hs[e];
+    } else {
+        for (int e = tid; e < kUpdRows * k; e += 256) {
+            if (e >= nel) {
+                Hn_s[e] = 0.f;
+                continue;
+            }
+            const int i = e / k;
+            const int c = e % k;
+            const int64_t gi = (int64_t)(row0 + i);
+            const float* p = a.part + gi * a.ldp + c;
+            float s = 0.f;
+            for (int sp = 0; sp < a.nsplit; ++sp) s += p[sp * a.pstride];
+            float P = s;
+            if (a.Pt) P = a.Pt[gi * k + c] + a.pscale * s;
+            float hk = 0.f;
+            const float* hrow = Hs + i * k;
+            for (int d = 0; d < k; ++d) hk = fmaf(hrow[d], Ks[d * k + c], hk);
+            const float h = hrow[c];
+            const float g = 4.f * (hk - P);
+            const float Gv = a.G[gi * k + c] + g * g;
+            const float hn = fmaxf(h - a.lr * g / (sqrtf(Gv) + a.eps), 0.f);
+            a.Gn[gi * k + c] = Gv;
+            a.Hn[gi * k + c] = hn;
+            Hn_s[e] = hn;
+            if (a.Ha) a.Ha[gi * k + c] = h;
+            if (a.Pa) a.Pa[gi * k + c] = P;
+            tr += (double)h * (double)P;
+        }
+    }
+    __syncthreads();
+    if (a.tr_part) {
+        const double t = block_sum256(tr, red);
+        if (tid == 0) a.tr_part[blockIdx.x] = t;
+    }
+    // partial Gram of the rows written (upper triangle, fp32 over <= 64 rows)
+    float* gp = a.gram_part + (int64_t)blockIdx.x * k * k;
+    for (int idx = tid; idx < k * k; idx += 256) {
+        const int x = idx / k;
+        const int y = idx % k;
+        if (x <= y) {
+            float s = 0.f;
+            for (int i = 0; i < kUpdRows; ++i) s = fmaf(Hn_s[i * k + x], Hn_s[i * k + y], s);
+            gp[idx] = s;
+        }
+    }
+}
+
+hipError_t launch_update(const UpdateArgs& a, hipStream_t st) {
+    const int nblk = (a.n + kUpdRows - 1) / kUpdRows;
+    const size_t sm = (size_t)(2 * kUpdRows * a.k + a.k * a.k) * sizeof(float);
+    if (sm > 65536) {
+        hipError_t e = hipFuncSetAttribute((const void*)update_kernel,
+                                           hipFuncAttributeMaxDynamicSharedMemorySize, (int)sm);
+        if (e != hipSuccess) return e;
+    }
+    hipLaunchKernelGGL(update_kernel, dim3(nblk), dim3(256), sm, st, a);
+    return hipGetLastError();
+}
+
+// ---- per-step finalisation ----------------------------------------------------
+// Workgroup x < k*k folds Gram entry x (upper triangle) over the update blocks;
+// workgroup k*k folds the trace partials. Each sum is split over 256 threads
+// in a fixed stride and combined by a fixed-order tree, so it is
+// deterministic. The last workgroup to finish (counted with an atomic ticket)
+// forms f_t = ||S||^2 - 2 tr + ||K_t||^2, runs the stop test, publishes
+// K_{t+1} and resets the ticket for the next step.
+__global__ __launch_bounds__(256) void finalize_kernel(FitDev* fd, double* f_trace, int t,
+                                                       int nblk, int k,
+                                                       const double* __restrict__ tr_part,
+                                                       const float* __restrict__ gram_part,
+                                                       int flags) {
+    if (fd->done) return;
+    __shared__ double red[4];
+    __shared__ int last;
+    const int tid = threadIdx.x;
+    const int wg = blockIdx.x;
+    const int kk = k * k;
+    if (wg < kk) {
+        const int x = wg / k;
+        const int y = wg % k;
+        if ((flags & 4) && x <= y) {
+            double s = 0.0;
+            for (int b = tid; b < nblk; b += 256) s += (double)gram_part[(int64_t)b * kk + wg];
+            s = block_sum256(s, red);
+            if (tid == 0) fd->Kd[wg] = s;
+        }
+    } else if (flags & 1) {
+        double s = 0.0;
+        for (int b = tid; b < nblk; b += 256) s += tr_part[b];
+        s = block_sum256(s, red);
+        if (tid == 0) fd->tr = s;
+    }
+    __threadfence();
+    if (tid == 0) last = (atomicAdd(&fd->ticket, 1u) == gridDim.x - 1);
+    __syncthreads();
+    if (!last) return;
+    __threadfence();
+    if (flags & 4) {
+        double k2 = 0.0;
+        for (int idx = tid; idx < kk; idx += 256) {
+            const int x = idx / k;
+            const int y = idx % k;
+            if (x <= y) {
+                const double s = ((volatile double*)fd->Kd)[idx];
+                fd->K[x * kMaxK + y] = (float)s;
+                fd->K[y * kMaxK + x] = (float)s;
+                k2 += (x == y ? 1.0 : 2.0) * s * s;
+            }
+        }
+        k2 = block_sum256(k2, red);
+        if (tid == 0) fd->K2next = k2;
+    }
+    if (tid == 0) {
+        if (flags & 8) {
+            // initial Gram only: no objective, no trace entry
+        } else if (flags & 1) {
+            const double tr = *((volatile double*)&fd->tr);
+            const double f = fd->S_fro2 - 2.0 * tr + fd->K2;
+            if (f_trace) f_trace[t] = f;
+            if (!isfinite(f)) {
+                fd->status = -4;
+                fd->done = 1;
+                fd->stop_iter = t;
+            } else if ((flags & 2) && fd->tol > 0.0 && fd->f_prev_valid &&
+                       fabs(fd->f_prev - f) < fd->tol * fabs(fd->f_prev)) {
+                fd->status = 1;
+                fd->done = 1;
+                fd->stop_iter = t;
+            }
+            fd->f_prev = f;
+            fd->f_prev_valid = 1;
+        } else {
+            if (f_trace) f_trace[t] = __builtin_nan("");
+            fd->f_prev_valid = 0;
+        }
+        if (flags & 4) fd->K2 = fd->K2next;
+        fd->ticket = 0u;
+    }
+}
+
+hipError_t launch_finalize(FitDev* fd, double* f_trace, int t, int nblk, int k,
+                           const double* tr_part, const float* gram_part, int flags,
+                           hipStream_t st) {
+    hipLaunchKernelGGL(finalize_kernel, dim3(k * k + 1), dim3(256), 0, st, fd, f_trace, t, nblk,
+                       k, tr_part, gram_part, flags);
+    return hipGetLastError();
+}
+
+// ---- labels (P1 "Factorizing with SymNMF": row-wise argmax) --------------------
+__global__ void labels_kernel(const float* __restrict__ H, int64_t n, int k,
+                              int32_t* __restrict__ out) {
+    const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (i >= n) return;
+    const float* h = H + i * k;
+    int best = 0;
+    float bv = h[0];
+    for (int c = 1; c < k; ++c) {
+        const float v = h[c];
+        if (v > bv) {  // strict: the lowest index wins ties
+            bv = v;
+            best = c;
+        }
+    }
+    out[i] = best;
+}
+hipError_t launch_labels(const float* H, int64_t n, int k, int32_t* labels, hipStream_t st) {
+    if (n <= 0) return hipSuccess;
+    hipLaunchKernelGGL(labels_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, H, n,
+                       k, labels);
+    return hipGetLastError();
+}
+
+__global__ void zero_rows_kernel(const float* __restrict__ H, int n, int k, int* out) {
+    const int i = blockIdx.x * blockDim.x + threadIdx.x;
+    if (i >= n) return;
+    bool z = true;
+    for (int c = 0; c < k; ++c) z = z && (H[(int64_t)i * k + c] == 0.f);
+    if (z) atomicAdd(out, 1);
+}
+hipError_t launch_count_zero_rows(const float* H, int n, int k, int* out, hipStream_t st) {
+    if (n <= 0) return hipSuccess;
+    hipLaunchKernelGGL(zero_rows_kernel, dim3((n + 255) / 256), dim3(256), 0, st, H, n, k, out);
+    return hipGetLastError();
+}
+
+// ---- probe helpers ---------------------------------------------------------------
+// C = A^T B partials over blocks of kCgRows rows; fp64 accumulation.
+constexpr int kCgRows = 512;
+constexpr int kCgChunk = 32;
+
+__global__ __launch_bounds__(256) void crossgram_kernel(const float* __restrict__ A,
+                                                        const float* __restrict__ B, int n, int w,
+                                                        double* __restrict__ part) {
+    extern __shared__ float cg[];
+    float* As = cg;                 // kCgChunk x w
+    float* Bs = cg + kCgChunk * w;  // kCgChunk x w
+    const int row0 = blockIdx.x * kCgRows;
+    const int rend = min(n, row0 + kCgRows);
+    const int tid = threadIdx.x;
+    // each thread owns entries idx = tid + 256 m of the w x w result
+    constexpr int kMaxOwn = (kMaxWidth * kMaxWidth + 255) / 256;
+    double acc[kMaxOwn];
+    const int own = (w * w + 255) / 256;
+#pragma unroll
+    for (int m = 0; m < kMaxOwn; ++m) acc[m] = 0.0;
+    for (int r0 = row0; r0 < rend; r0 += kCgChunk) {
+        const int rows = min(kCgChunk, rend - r0);
+        __syncthreads();
+        for (int e = tid; e < kCgChunk * w; e += 256) {
+            const int i = e / w;
+            As[e] = (i < rows) ? A[(int64_t)(r0 + i) * w + (e % w)] : 0.f;
+            Bs[e] = (i < rows) ? B[(int64_t)(r0 + i) * w + (e % w)] : 0.f;
+        }
+        __syncthreads();
+#pragma unroll
+        for (int m = 0; m < kMaxOwn; ++m) {
+            if (m < own) {
+                const int idx = tid + 256 * m;
+                if (idx < w * w) {
+                    const int x = idx / w;
+                    const int y = idx % w;
+                    float s = 0.f;  // <= 32 terms in fp32, then fp64
+                    for (int i = 0; i < kCgChunk; ++i) s = fmaf(As[i * w + x], Bs[i * w + y], s);
+                    acc[m] += (double)s;
+                }
+            }
+        }
+    }
+    double* out = part + (int64_t)blockIdx.x * w * w;
+#pragma unroll
+    for (int m = 0; m < kMaxOwn; ++m) {
+        const int idx = tid + 256 * m;
+        if (m < own && idx < w * w) out[idx] = acc[m];
+    }
+}
+
+__global__ void crossgram_final_kernel(const double* __restrict__ part, int nblk, int ww,
+                                       double* __restrict__ C) {
+    const int idx = blockIdx.x * blockDim.x + threadIdx.x;
+    if (idx >= ww) return;
+    double s = 0.0;
+    for (int b = 0; b < nblk; ++b) s += part[(int64_t)b * ww + idx];
+    C[idx] = s;
+}
+
+int crossgram_blocks(int n) { return (n + kCgRows - 1) / kCgRows; }
+
+hipError_t launch_crossgram(const float* A, const float* B, int n, int w, double* part,
+                            int nblk, double* C, hipStream_t st) {
+    const size_t sm = (size_t)2 * kCgChunk * w * sizeof(float);
+    hipLaunchKernelGGL(crossgram_kernel, dim3(nblk), dim3(256), sm, st, A, B, n, w, part);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    const int ww = w * w;
+    hipLaunchKernelGGL(crossgram_final_kernel, dim3((ww + 255) / 256), dim3(256), 0, st, part,
+                       nblk, ww, C);
+    return hipGetLastError();
+}
+
+// Q = Y M, one thread per output element, M staged in LDS.
+__global__ __launch_bounds__(256) void rowmat_kernel(const float* __restrict__ Y,
+                                                     const float* __restrict__ M, int n, int w,
+                                                     float* __restrict__ Q) {
+    extern __shared__ float Ms[];
+    for (int e = threadIdx.x; e < w * w; e += 256) Ms[e] = M[e];
+    __syncthreads();
+    const int64_t total = (int64_t)n * w;
+    for (int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x; e < total;
+         e += (int64_t)gridDim.x * 256) {
+        const int64_t i = e / w;
+        const int c = (int)(e % w);
+        const float* y = Y + i * w;
+        float s = 0.f;
+        for (int d = 0; d < w; ++d) s = fmaf(y[d], Ms[d * w + c], s);
+        Q[e] = s;
+    }
+}
+hipError_t launch_rowmat(const float* Y, const float* M, int n, int w, float* Q, hipStream_t st) {
+    const int64_t total = (int64_t)n * w;
+    int64_t blocks = (total + 255) / 256;
+    if (blocks > 4096) blocks = 4096;
+    hipLaunchKernelGGL(rowmat_kernel, dim3((unsigned)blocks), dim3(256),
+                       (size_t)w * w * sizeof(float), st, Y, M, n, w, Q);
+    return hipGetLastError();
+}
+
+}  // namespace symnmf

@@ -1,0 +1,129 @@
+// Internal launcher interface between the host controller (symnmf.cpp) and the
+// gfx950 kernels (k_*.hip). Every launcher enqueues on `st` and returns the
+// hipError_t of the launch.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace symnmf {
+
+constexpr int kMaxK = 64;         // widest factor the fit supports
+constexpr int kMaxWidth = 128;    // widest S.H pass (probe subspace)
+constexpr int kShTileCols = 256;  // columns of S per S.H workgroup (4 waves x 64)
+constexpr int kUpdRows = 64;      // rows per workgroup of the fused update kernel
+constexpr int kGramTile = 128;    // S-build workgroup tile (2 x 2 waves of 64 x 64)
+
+constexpr int kMaxSplits = 16;   // row splits of one S.H pass (fixed-order sum)
+
+// Which rows of S one split of the S.H pass streams.
+//  contiguous (blocks == nullptr): split s covers
+//      [s * rows_per_split, min(n, (s + 1) * rows_per_split))
+//  sampled, sub > 1: split s covers rows [s%sub * seg, +seg) of block
+//      blocks[s / sub] (clipped to the block and to n)
+//  sampled, sub == 1: split s covers the whole blocks
+//      blocks[s * bps .. min(nsel, (s + 1) * bps) - 1]
+struct RowPlan {
+    int n;
+    int rows_per_split;
+    const int* blocks;
+    int nsel;
+    int block_rows;
+    int sub;
+    int seg;
+    int bps;
+};
+
+// Device state of one fit, in the caller's workspace.
+struct FitDev {
+    double S_fro2;
+    double K2;          // ||H_t^T H_t||_F^2 for the current H_t
+    double f_prev;      // last exact objective
+    double tol;         // relative convergence tolerance (0: no test)
+    int f_prev_valid;
+    int done;           // once set, every later kernel of the fit returns at once
+    int stop_iter;
+    int status;         // 0 running, 1 converged, -4 non-finite objective
+    unsigned int ticket;  // finalisation: workgroups done this step
+    double tr;            // finalisation scratch: tr(H_t^T P_t)
+    double K2next;        // finalisation scratch: ||H_{t+1}^T H_{t+1}||^2
+    double Kd[kMaxK * kMaxK];  // finalisation scratch: Gram entries (fp64)
+    float K[kMaxK * kMaxK];    // H_t^T H_t (fp32, full symmetric, ld kMaxK)
+};
+
+// ---- S.H pass ---------------------------------------------------------------
+// part[s][i][c] (ld ldp = round_up(width, 4), split stride n*ldp) =
+//   sum over rows j of split s of S[j][i] * (X[j][c] - Xa[j][c])   (Xa nullable)
+// which is (S X)[i][c] restricted to those rows, for symmetric S.
+hipError_t launch_sh_panel(const float* S, int64_t lds, const float* X, const float* Xa,
+                           int width, const RowPlan& rp, int nsplit, float* part, int ldp,
+                           hipStream_t st);
+// P[i][c] = sum_s part[s][i][c] (c < width, ld width); if Hdot: tr_part[b] =
+// sum over the rows of block b of <Hdot_i, P_i> (fp64). Blocks of kUpdRows rows.
+hipError_t launch_reduce_partials(const float* part, int nsplit, int n, int width, int ldp,
+                                  float* P, const float* Hdot, double* tr_part, hipStream_t st);
+
+// ---- fit --------------------------------------------------------------------
+hipError_t launch_s_stats(const float* S, int64_t lds, int n, double* part2, hipStream_t st);
+hipError_t launch_s_stats_final(const double* part2, int nblk, double* out2, hipStream_t st);
+hipError_t launch_init_uniform(float* H, int64_t count, float scale, float shift, uint64_t seed,
+                               hipStream_t st);
+hipError_t launch_fill(float* p, int64_t count, float v, hipStream_t st);
+hipError_t launch_copy(float* dst, const float* src, int64_t count, hipStream_t st);
+
+struct UpdateArgs {
+    int n, k, ldp;
+    const float* part;   // nsplit partial products (nullable for gram-only)
+    int nsplit;
+    int64_t pstride;
+    const float* Pt;     // Block-SVRG anchor product P~ (nullable: exact pass)
+    float pscale;        // nb / |B|
+    const float* H;      // H_t
+    const float* G;      // G_t
+    float* Hn;           // H_{t+1}
+    float* Gn;           // G_{t+1}
+    float* Ha;           // anchor H~ <- H_t (nullable)
+    float* Pa;           // anchor P~ <- P_t (nullable)
+    FitDev* fd;
+    float lr, eps;
+    double* tr_part;     // per block <H_t, P_t> (nullable)
+    float* gram_part;    // per block partial Gram of the rows written (k x k)
+    int gram_only;       // 1: no update, Gram partials of H
+};
+hipError_t launch_update(const UpdateArgs& a, hipStream_t st);
+// flags: 1 exact objective this step, 2 convergence test, 4 fold Gram partials into K
+hipError_t launch_finalize(FitDev* fd, double* f_trace, int t, int nblk, int k,
+                           const double* tr_part, const float* gram_part, int flags,
+                           hipStream_t st);
+hipError_t launch_count_zero_rows(const float* H, int n, int k, int* out, hipStream_t st);
+hipError_t launch_labels(const float* H, int64_t n, int k, int32_t* labels, hipStream_t st);
+
+// ---- probe helpers ----------------------------------------------------------
+// C = A^T B (w x w, fp64) for n x w matrices A, B (ld w): per-block partials then
+// a fixed-order reduction into C.
+hipError_t launch_crossgram(const float* A, const float* B, int n, int w, double* part,
+                            int nblk, double* C, hipStream_t st);
+int crossgram_blocks(int n);
+// Q[i][:] = Y[i][:] M (M w x w fp32, row-major)
+hipError_t launch_rowmat(const float* Y, const float* M, int n, int w, float* Q, hipStream_t st);
+
+// ---- S build ----------------------------------------------------------------
+// Z (Tp x ldz): standardised columns (c < n), zero padding; flags[0] |= 1 on a
+// non-finite input, flags[1] |= 1 on a constant column.
+hipError_t launch_standardize(const float* X, int T, int n, int64_t ldx, float* Z, int Tp,
+                              int64_t ldz, int* flags, hipStream_t st);
+hipError_t launch_tpdm_ranks(const float* X, int T, int n, int64_t ldx, int* R, int* hist,
+                             int* flags, hipStream_t st);
+hipError_t launch_tpdm_select(const int* hist, int T, int m, double* radius, int* sel,
+                              hipStream_t st);
+hipError_t launch_tpdm_theta(const int* R, int T, int n, const int* sel, const double* radius,
+                             int m, int mp, float* Theta, int64_t ldz, hipStream_t st);
+// S = scale * (|A^T A| if absval else A^T A), A = Z (Kp x ldz, Kp % 4 == 0),
+// upper-triangle tiles mirrored; part2[tile] = partial ||S||^2 (fp64).
+hipError_t launch_gram_build(const float* Z, int Kp, int64_t ldz, int n, float scale, int absval,
+                             float* S, int64_t lds, double* part2, int64_t* ntiles_out,
+                             hipStream_t st);
+int64_t gram_build_tiles(int n);
+hipError_t launch_sum_doubles(const double* part, int64_t count, double* out, hipStream_t st);
+
+}  // namespace symnmf

@@ -1,0 +1,912 @@
+// libsymnmf host side: the C ABI of include/symnmf.h, argument validation,
+// workspace layout, the AdaptGrow controller, the spectral probe's small fp64
+// algebra and kernel timing. Every step of the path runs in the gfx950
+// kernels of k_*.hip; this file only sequences launches and handles scalars.
+//
+// Pages: P1 "GPU-Accelerated Clustering for Financial Instruments at Scale";
+// P2 "GPU-Accelerated SymNMF Clustering Scales to a Million Financial
+// Instruments" (AdaGrad update, AdaptGrow sketch); P3 the SymNMF study
+// abstract on the paper-card page "GEM-KMeans: ...".
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <chrono>
+#include <cmath>
+#include <cstddef>
+#include <cstring>
+#include <mutex>
+#include <vector>
+
+#include "common.h"
+#include "kernels.h"
+#include "symnmf.h"
+
+using namespace symnmf;
+
+namespace {
+
+constexpr size_t kAlign = 256;
+
+inline size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+inline int64_t round_up(int64_t x, int64_t m) { return (x + m - 1) / m * m; }
+inline int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+// Bump allocator over the caller's workspace. With base == nullptr it only
+// measures.
+struct Carve {
+    char* base;
+    size_t off = 0;
+    explicit Carve(void* b) : base(static_cast<char*>(b)) {}
+    template <class T>
+    T* take(size_t count) {
+        T* p = base ? reinterpret_cast<T*>(base + off) : nullptr;
+        off = align_up(off + count * sizeof(T));
+        return p;
+    }
+};
+
+// ---------------------------------------------------------------------------
+// kernel timing
+struct ProfEntry {
+    hipEvent_t a, b;
+    int which;
+    double bytes;
+};
+struct Prof {
+    std::mutex mu;
+    bool on = false;
+    std::vector<ProfEntry> pending;
+    int64_t launches[SYMNMF_PROF_COUNT] = {};
+    double ms[SYMNMF_PROF_COUNT] = {};
+    double bytes[SYMNMF_PROF_COUNT] = {};
+};
+Prof& prof() {
+    static Prof p;
+    return p;
+}
+
+struct ProfScope {
+    hipEvent_t a = nullptr, b = nullptr;
+    hipStream_t st;
+    int which;
+    double bytes;
+    ProfScope(int w, double by, hipStream_t s) : st(s), which(w), bytes(by) {
+        Prof& p = prof();
+        if (!p.on) return;
+        if (hipEventCreate(&a) != hipSuccess || hipEventCreate(&b) != hipSuccess) {
+            a = b = nullptr;
+            return;
+        }
+        (void)hipEventRecord(a, st);
+    }
+    ~ProfScope() {
+        if (!a) return;
+        (void)hipEventRecord(b, st);
+        Prof& p = prof();
+        std::lock_guard<std::mutex> g(p.mu);
+        p.pending.push_back({a, b, which, bytes});
+    }
+};
+
+void prof_drain() {
+    Prof& p = prof();
+    std::lock_guard<std::mutex> g(p.mu);
+    for (auto& e : p.pending) {
+        (void)hipEventSynchronize(e.b);
+        float ms = 0.f;
+        if (hipEventElapsedTime(&ms, e.a, e.b) == hipSuccess) {
+            p.launches[e.which] += 1;
+            p.ms[e.which] += ms;
+            p.bytes[e.which] += e.bytes;
+        }
+        (void)hipEventDestroy(e.a);
+        (void)hipEventDestroy(e.b);
+    }
+    p.pending.clear();
+}
+
+#define HIPCHK(x)                                   \
+    do {                                            \
+        hipError_t _e = (x);                        \
+        if (_e != hipSuccess) return SYMNMF_E_HIP;  \
+    } while (0)
+
+inline hipStream_t as_stream(void* s) { return static_cast<hipStream_t>(s); }
+inline bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+// ---------------------------------------------------------------------------
+// S.H pass planning
+struct FullPlan {
+    RowPlan rp;
+    int nsplit;
+};
+FullPlan full_plan(int n) {
+    // at most 16 splits, at least 64 rows each: one output accumulates at most
+    // ceil(n/16) rows in fp32 before the fixed-order split sum
+    int rps = (int)round_up(std::max<int64_t>(64, cdiv(n, kMaxSplits)), 4);
+    FullPlan fp;
+    fp.nsplit = (int)cdiv(n, rps);
+    fp.rp = RowPlan{n, rps, nullptr, 0, 0, 1, 0, 1};
+    return fp;
+}
+FullPlan sampled_plan(int n, const int* blocks_dev, int nsel, int block_rows) {
+    FullPlan fp;
+    RowPlan rp{n, 0, blocks_dev, nsel, block_rows, 1, 0, 1};
+    if (nsel < kMaxSplits) {
+        int sub = std::max(1, std::min(kMaxSplits / nsel, block_rows / 64));
+        rp.sub = sub;
+        rp.seg = (int)round_up(cdiv(block_rows, sub), 4);
+        rp.bps = 1;
+        fp.nsplit = nsel * sub;
+    } else {
+        rp.sub = 1;
+        rp.bps = (int)cdiv(nsel, kMaxSplits);
+        fp.nsplit = (int)cdiv(nsel, rp.bps);
+    }
+    fp.rp = rp;
+    return fp;
+}
+inline int ldp_of(int width) { return (int)round_up(width, 4); }
+
+// ---------------------------------------------------------------------------
+// Small dense fp64 algebra for the probe (host side; w <= 128).
+
+// Cyclic Jacobi eigen-decomposition of a symmetric w x w matrix A (row-major,
+// destroyed). Eigenvalues to ev; eigenvectors (columns of V) if V != nullptr.
+void jacobi_eig(int w, std::vector<double>& A, std::vector<double>& ev, std::vector<double>* V) {
+    if (V) {
+        V->assign((size_t)w * w, 0.0);
+        for (int i = 0; i < w; ++i) (*V)[(size_t)i * w + i] = 1.0;
+    }
+    for (int sweep = 0; sweep < 100; ++sweep) {
+        double off = 0.0, diag = 0.0;
+        for (int i = 0; i < w; ++i)
+            for (int j = 0; j < w; ++j) {
+                const double a = A[(size_t)i * w + j];
+                if (i != j) off += a * a; else diag += a * a;
+            }
+        if (off <= 1e-30 * diag || off == 0.0) break;
+        for (int p = 0; p < w - 1; ++p)
+            for (int q = p + 1; q < w; ++q) {
+                const double apq = A[(size_t)p * w + q];
+                if (apq == 0.0) continue;
+                const double app = A[(size_t)p * w + p], aqq = A[(size_t)q * w + q];
+                const double theta = (aqq - app) / (2.0 * apq);
+                const double t = (theta >= 0 ? 1.0 : -1.0) /
+                                 (std::fabs(theta) + std::sqrt(theta * theta + 1.0));
+                const double c = 1.0 / std::sqrt(t * t + 1.0), s = t * c;
+                for (int r = 0; r < w; ++r) {  // columns p, q
+                    const double arp = A[(size_t)r * w + p], arq = A[(size_t)r * w + q];
+                    A[(size_t)r * w + p] = c * arp - s * arq;
+                    A[(size_t)r * w + q] = s * arp + c * arq;
+                }
+                for (int r = 0; r < w; ++r) {  // rows p, q
+                    const double apr = A[(size_t)p * w + r], aqr = A[(size_t)q * w + r];
+                    A[(size_t)p * w + r] = c * apr - s * aqr;
+                    A[(size_t)q * w + r] = s * apr + c * aqr;
+                }
+                if (V)
+                    for (int r = 0; r < w; ++r) {
+                        const double vrp = (*V)[(size_t)r * w + p], vrq = (*V)[(size_t)r * w + q];
+                        (*V)[(size_t)r * w + p] = c * vrp - s * vrq;
+                        (*V)[(size_t)r * w + q] = s * vrp + c * vrq;
+                    }
+            }
+    }
+    ev.resize(w);
+    for (int i = 0; i < w; ++i) ev[i] = A[(size_t)i * w + i];
+}
+
+// G = R^T R with R upper triangular; false on a pivot below rel * G_jj.
+bool cholesky_upper(int w, const std::vector<double>& G, std::vector<double>& R, double rel) {
+    R.assign((size_t)w * w, 0.0);
+    for (int j = 0; j < w; ++j) {
+        double d = G[(size_t)j * w + j];
+        for (int i = 0; i < j; ++i) d -= R[(size_t)i * w + j] * R[(size_t)i * w + j];
+        if (!(d > rel * G[(size_t)j * w + j]) || !std::isfinite(d)) return false;
+        const double rjj = std::sqrt(d);
+        R[(size_t)j * w + j] = rjj;
+        for (int c = j + 1; c < w; ++c) {
+            double s = G[(size_t)j * w + c];
+            for (int i = 0; i < j; ++i) s -= R[(size_t)i * w + j] * R[(size_t)i * w + c];
+            R[(size_t)j * w + c] = s / rjj;
+        }
+    }
+    return true;
+}
+
+// inverse of an upper-triangular matrix
+void upper_inverse(int w, const std::vector<double>& R, std::vector<double>& Ri) {
+    Ri.assign((size_t)w * w, 0.0);
+    for (int c = 0; c < w; ++c) {
+        Ri[(size_t)c * w + c] = 1.0 / R[(size_t)c * w + c];
+        for (int r = c - 1; r >= 0; --r) {
+            double s = 0.0;
+            for (int m = r + 1; m <= c; ++m) s += R[(size_t)r * w + m] * Ri[(size_t)m * w + c];
+            Ri[(size_t)r * w + c] = -s / R[(size_t)r * w + r];
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// workspace layouts
+
+struct ShLayout {
+    float* part;
+    double* tr_part;
+    double* tr_out;
+};
+size_t sh_layout(void* ws, int64_t n, int width, ShLayout* L) {
+    Carve c(ws);
+    FullPlan fp = full_plan((int)n);
+    ShLayout l;
+    l.part = c.take<float>((size_t)fp.nsplit * n * ldp_of(width));
+    l.tr_part = c.take<double>((size_t)cdiv(n, kUpdRows));
+    l.tr_out = c.take<double>(1);
+    if (L) *L = l;
+    return c.off;
+}
+
+struct ProbeLayout {
+    float *Q, *Y, *part, *M;
+    double *cg_part, *C;
+};
+int probe_width(int p) { return (int)round_up(p + 16, 16); }
+size_t probe_layout(void* ws, int64_t n, int p, ProbeLayout* L) {
+    Carve c(ws);
+    const int w = probe_width(p);
+    FullPlan fp = full_plan((int)n);
+    ProbeLayout l;
+    l.Q = c.take<float>((size_t)n * w);
+    l.Y = c.take<float>((size_t)n * w);
+    l.part = c.take<float>((size_t)fp.nsplit * n * ldp_of(w));
+    l.M = c.take<float>((size_t)w * w);
+    l.cg_part = c.take<double>((size_t)crossgram_blocks((int)n) * w * w);
+    l.C = c.take<double>((size_t)w * w);
+    if (L) *L = l;
+    return c.off;
+}
+
+struct FitLayout {
+    FitDev* fd;
+    double* f_trace;
+    float *Hb[2], *Gb[2], *Ha, *Pa, *part, *gram_part;
+    double *tr_part, *stats_part, *stats_out;
+    int *blocks, *zero_rows;
+};
+size_t fit_layout(void* ws, int64_t n, int k, int max_iters, int block_rows, FitLayout* L) {
+    Carve c(ws);
+    const int nb = (int)cdiv(n, block_rows);
+    const int nblk = (int)cdiv(n, kUpdRows);
+    FitLayout l;
+    l.fd = c.take<FitDev>(1);
+    l.f_trace = c.take<double>((size_t)std::max(1, max_iters));
+    for (int i = 0; i < 2; ++i) l.Hb[i] = c.take<float>((size_t)n * k);
+    for (int i = 0; i < 2; ++i) l.Gb[i] = c.take<float>((size_t)n * k);
+    l.Ha = c.take<float>((size_t)n * k);
+    l.Pa = c.take<float>((size_t)n * k);
+    l.part = c.take<float>((size_t)kMaxSplits * n * ldp_of(k));
+    l.gram_part = c.take<float>((size_t)nblk * k * k);
+    l.tr_part = c.take<double>((size_t)nblk);
+    l.stats_part = c.take<double>((size_t)2 * cdiv(n, 64));
+    l.stats_out = c.take<double>(2);
+    l.blocks = c.take<int>((size_t)2 * nb + 16);
+    l.zero_rows = c.take<int>(1);
+    if (L) *L = l;
+    return c.off;
+}
+
+struct BuildLayout {
+    float* Z;  // Z or Theta
+    int *R, *hist, *sel, *flags;
+    double *radius, *part2, *fro;
+};
+size_t build_layout(void* ws, int kind, int64_t T, int64_t n, BuildLayout* L) {
+    Carve c(ws);
+    const int64_t ldz = round_up(n, kGramTile);
+    BuildLayout l{};
+    if (kind == SYMNMF_ABSCORR) {
+        l.Z = c.take<float>((size_t)round_up(T, 4) * ldz);
+    } else {
+        // Theta needs m_p = round_up(ceil(tail_frac T), 4) <= round_up(T, 4) rows
+        l.Z = c.take<float>((size_t)round_up(T, 4) * ldz);
+        l.R = c.take<int>((size_t)T * n);
+        l.hist = c.take<int>((size_t)T * (T + 1));
+        l.sel = c.take<int>((size_t)T);
+        l.radius = c.take<double>((size_t)T);
+    }
+    l.flags = c.take<int>(2);
+    l.part2 = c.take<double>((size_t)gram_build_tiles((int)n));
+    l.fro = c.take<double>(1);
+    if (L) *L = l;
+    return c.off;
+}
+
+bool ws_ok(void* ws, size_t ws_bytes, size_t need) {
+    return ws != nullptr && aligned(ws, kAlign) && ws_bytes >= need;
+}
+
+}  // namespace
+
+// ===========================================================================
+extern "C" {
+
+int symnmf_abi_version(void) { return SYMNMF_ABI_VERSION; }
+
+const char* symnmf_status_string(int status) {
+    switch (status) {
+        case SYMNMF_OK: return "ok";
+        case SYMNMF_W_NOT_CONVERGED: return "not converged within max_iters";
+        case SYMNMF_E_INVALID: return "invalid argument";
+        case SYMNMF_E_WORKSPACE: return "workspace missing, misaligned or too small";
+        case SYMNMF_E_HIP: return "HIP runtime error";
+        case SYMNMF_E_NONFINITE: return "non-finite value in input or objective";
+        case SYMNMF_E_DEGENERATE: return "constant column: correlation undefined";
+        default: return "unknown status";
+    }
+}
+
+void symnmf_fit_params_default(symnmf_fit_params* p) {
+    if (!p) return;
+    std::memset(p, 0, sizeof(*p));
+    p->solver = SYMNMF_AUTO;
+    p->max_iters = 2000;
+    p->lr = 0.0;
+    p->eps = 1e-8;
+    p->block_rows = 1024;
+    p->init = SYMNMF_INIT_SCALE_MATCHED;
+    p->phi0 = 0.0;
+    p->gap_threshold = 5.0;
+    p->tol_rel = 1e-6;
+    p->stall_tol = 1e-3;
+    p->init_scale = 0.1;
+    p->seed = 0;
+    p->check_every = 16;
+    p->resume = 0;
+}
+
+size_t symnmf_workspace_bytes(int op, int64_t n, int32_t k_or_p, int64_t T,
+                              const symnmf_fit_params* prm) {
+    if (n < 1 || n > INT32_MAX / 2) return 0;
+    switch (op) {
+        case SYMNMF_OP_BUILD_S:
+            if (T < 2 || T > 65536) return 0;
+            return std::max(build_layout(nullptr, SYMNMF_ABSCORR, T, n, nullptr),
+                            build_layout(nullptr, SYMNMF_TPDM, T, n, nullptr));
+        case SYMNMF_OP_PROBE:
+            if (k_or_p < 1 || probe_width(k_or_p) > kMaxWidth) return 0;
+            return probe_layout(nullptr, n, k_or_p, nullptr);
+        case SYMNMF_OP_SH:
+            if (k_or_p < 1 || k_or_p > kMaxWidth) return 0;
+            return sh_layout(nullptr, n, k_or_p, nullptr);
+        case SYMNMF_OP_FIT: {
+            if (k_or_p < 1 || k_or_p > kMaxK) return 0;
+            symnmf_fit_params d;
+            symnmf_fit_params_default(&d);
+            const symnmf_fit_params* p = prm ? prm : &d;
+            if (p->max_iters < 0 || p->block_rows < 4) return 0;
+            return fit_layout(nullptr, n, k_or_p, p->max_iters, p->block_rows, nullptr);
+        }
+        default: return 0;
+    }
+}
+
+void symnmf_profile_enable(int on) {
+    Prof& p = prof();
+    std::lock_guard<std::mutex> g(p.mu);
+    p.on = on != 0;
+}
+void symnmf_profile_reset(void) {
+    prof_drain();
+    Prof& p = prof();
+    std::lock_guard<std::mutex> g(p.mu);
+    for (int i = 0; i < SYMNMF_PROF_COUNT; ++i) {
+        p.launches[i] = 0;
+        p.ms[i] = 0.0;
+        p.bytes[i] = 0.0;
+    }
+}
+int symnmf_profile_read(int which, int64_t* launches, double* total_ms, double* total_bytes) {
+    if (which < 0 || which >= SYMNMF_PROF_COUNT) return SYMNMF_E_INVALID;
+    prof_drain();
+    Prof& p = prof();
+    std::lock_guard<std::mutex> g(p.mu);
+    if (launches) *launches = p.launches[which];
+    if (total_ms) *total_ms = p.ms[which];
+    if (total_bytes) *total_bytes = p.bytes[which];
+    return SYMNMF_OK;
+}
+
+// ---------------------------------------------------------------------------
+int symnmf_labels(const float* H, int64_t n, int32_t k, int32_t* labels, void* hip_stream) {
+    if (!H || !labels || n < 0 || k < 1 || n > INT32_MAX) return SYMNMF_E_INVALID;
+    if (n == 0) return SYMNMF_OK;
+    HIPCHK(launch_labels(H, n, k, labels, as_stream(hip_stream)));
+    return SYMNMF_OK;
+}
+
+// ---------------------------------------------------------------------------
+int symnmf_sh(const float* S, int64_t n, int64_t lds, const float* H, int32_t k, float* P,
+              double* tr_host, void* ws, size_t ws_bytes, void* hip_stream) {
+    if (!S || !H || !P || n < 1 || n > INT32_MAX / 2 || k < 1 || k > kMaxWidth || lds < n ||
+        lds % 4 || !aligned(S, 16) || !aligned(P, 4))
+        return SYMNMF_E_INVALID;
+    const size_t need = sh_layout(nullptr, n, k, nullptr);
+    if (!ws_ok(ws, ws_bytes, need)) return SYMNMF_E_WORKSPACE;
+    ShLayout L;
+    sh_layout(ws, n, k, &L);
+    hipStream_t st = as_stream(hip_stream);
+    FullPlan fp = full_plan((int)n);
+    const int ldp = ldp_of(k);
+    {
+        ProfScope ps(SYMNMF_PROF_SH_FULL, 4.0 * n * (double)n + 8.0 * n * k, st);
+        HIPCHK(launch_sh_panel(S, lds, H, nullptr, k, fp.rp, fp.nsplit, L.part, ldp, st));
+    }
+    HIPCHK(launch_reduce_partials(L.part, fp.nsplit, (int)n, k, ldp, P, H, L.tr_part, st));
+    if (tr_host) {
+        HIPCHK(launch_sum_doubles(L.tr_part, cdiv(n, kUpdRows), L.tr_out, st));
+        HIPCHK(hipMemcpyAsync(tr_host, L.tr_out, sizeof(double), hipMemcpyDeviceToHost, st));
+        HIPCHK(hipStreamSynchronize(st));
+    }
+    return SYMNMF_OK;
+}
+
+// ---------------------------------------------------------------------------
+int symnmf_build_S(int kind, const float* X, int64_t T, int64_t n, int64_t ldx, float tail_frac,
+                   float* S, int64_t lds, double* S_fro2_host, void* ws, size_t ws_bytes,
+                   void* hip_stream) {
+    if ((kind != SYMNMF_ABSCORR && kind != SYMNMF_TPDM) || !X || !S || T < 2 || T > 65536 ||
+        n < 1 || n > INT32_MAX / 2 || ldx < n || lds < n || lds % 4 || !aligned(S, 16))
+        return SYMNMF_E_INVALID;
+    if (kind == SYMNMF_TPDM && !(tail_frac > 0.f && tail_frac <= 1.f)) return SYMNMF_E_INVALID;
+    const size_t need = build_layout(nullptr, kind, T, n, nullptr);
+    if (!ws_ok(ws, ws_bytes, need)) return SYMNMF_E_WORKSPACE;
+    BuildLayout L;
+    build_layout(ws, kind, T, n, &L);
+    hipStream_t st = as_stream(hip_stream);
+    const int64_t ldz = round_up(n, kGramTile);
+    HIPCHK(launch_fill(reinterpret_cast<float*>(L.flags), 2, 0.f, st));
+    int Kp = 0;
+    float scale = 1.f;
+    int absval = 1;
+    if (kind == SYMNMF_ABSCORR) {
+        Kp = (int)round_up(T, 4);
+        HIPCHK(launch_standardize(X, (int)T, (int)n, ldx, L.Z, Kp, ldz, L.flags, st));
+    } else {
+        // m = ceil(tail_frac T) extreme days
+        int m = (int)std::ceil((double)tail_frac * (double)T - 1e-4);
+        m = std::max(1, std::min((int)T, m));
+        Kp = (int)round_up(m, 4);
+        HIPCHK(launch_fill(reinterpret_cast<float*>(L.hist), T * (T + 1), 0.f, st));
+        HIPCHK(launch_fill(reinterpret_cast<float*>(L.sel), T, 0.f, st));
+        HIPCHK(launch_tpdm_ranks(X, (int)T, (int)n, ldx, L.R, L.hist, L.flags, st));
+        int fl[2] = {0, 0};
+        HIPCHK(hipMemcpyAsync(fl, L.flags, sizeof(fl), hipMemcpyDeviceToHost, st));
+        HIPCHK(hipStreamSynchronize(st));
+        if (fl[0]) return SYMNMF_E_NONFINITE;
+        HIPCHK(launch_tpdm_select(L.hist, (int)T, m, L.radius, L.sel, st));
+        HIPCHK(launch_tpdm_theta(L.R, (int)T, (int)n, L.sel, L.radius, m, Kp, L.Z, ldz, st));
+        scale = (float)(1.0 / (double)m);
+        absval = 0;
+    }
+    int flags[2] = {0, 0};
+    HIPCHK(hipMemcpyAsync(flags, L.flags, sizeof(flags), hipMemcpyDeviceToHost, st));
+    HIPCHK(hipStreamSynchronize(st));
+    if (flags[0]) return SYMNMF_E_NONFINITE;
+    if (flags[1]) return SYMNMF_E_DEGENERATE;
+    int64_t ntiles = 0;
+    {
+        // algorithmic traffic: S written once (4 n^2 bytes) plus the panels read
+        ProfScope ps(SYMNMF_PROF_BUILD_GRAM, 4.0 * n * (double)n + 4.0 * Kp * (double)n, st);
+        HIPCHK(launch_gram_build(L.Z, Kp, ldz, (int)n, scale, absval, S, lds, L.part2, &ntiles,
+                                 st));
+    }
+    if (S_fro2_host) {
+        HIPCHK(launch_sum_doubles(L.part2, ntiles, L.fro, st));
+        HIPCHK(hipMemcpyAsync(S_fro2_host, L.fro, sizeof(double), hipMemcpyDeviceToHost, st));
+        HIPCHK(hipStreamSynchronize(st));
+    }
+    return SYMNMF_OK;
+}
+
+// ---------------------------------------------------------------------------
+namespace {
+
+// Q <- orthonormal basis of span(Y) (n x w) by two rounds of Cholesky QR; a
+// round whose Gram is numerically singular (rank-deficient S, e.g. a TPDM of
+// rank m < w) falls back to Q = Y V diag(1/sqrt(max(mu, tau))) from the Gram
+// eigenpairs, which keeps the well-determined directions orthonormal and
+// leaves the null directions near zero. On return `Q` holds the basis (the two
+// buffers may be swapped).
+int orthonormalize(float*& Y, float*& Q, int n, int w, ProbeLayout& L, hipStream_t st) {
+    const int nblk = crossgram_blocks(n);
+    std::vector<double> G((size_t)w * w), R, Ri, V, ev;
+    std::vector<float> M((size_t)w * w);
+    for (int round = 0; round < 2; ++round) {
+        HIPCHK(launch_crossgram(Y, Y, n, w, L.cg_part, nblk, L.C, st));
+        HIPCHK(hipMemcpyAsync(G.data(), L.C, sizeof(double) * w * w, hipMemcpyDeviceToHost, st));
+        HIPCHK(hipStreamSynchronize(st));
+        for (double v : G)
+            if (!std::isfinite(v)) return SYMNMF_E_NONFINITE;
+        for (int i = 0; i < w; ++i)
+            for (int j = i + 1; j < w; ++j) {
+                const double s = 0.5 * (G[(size_t)i * w + j] + G[(size_t)j * w + i]);
+                G[(size_t)i * w + j] = G[(size_t)j * w + i] = s;
+            }
+        if (cholesky_upper(w, G, R, 1e-10)) {
+            upper_inverse(w, R, Ri);
+            for (size_t e = 0; e < M.size(); ++e) M[e] = (float)Ri[e];
+        } else {
+            std::vector<double> A = G;
+            jacobi_eig(w, A, ev, &V);
+            double mx = 0.0;
+            for (double v : ev) mx = std::max(mx, v);
+            const double tau = std::max(1e-300, 1e-12 * mx);
+            for (int r = 0; r < w; ++r)
+                for (int c = 0; c < w; ++c)
+                    M[(size_t)r * w + c] = (float)(V[(size_t)r * w + c] / std::sqrt(std::max(ev[c], tau)));
+        }
+        HIPCHK(hipMemcpyAsync(L.M, M.data(), sizeof(float) * w * w, hipMemcpyHostToDevice, st));
+        HIPCHK(launch_rowmat(Y, L.M, n, w, Q, st));
+        HIPCHK(hipStreamSynchronize(st));  // M's host copy must outlive the transfer
+        std::swap(Y, Q);
+    }
+    std::swap(Y, Q);
+    return SYMNMF_OK;
+}
+
+}  // namespace
+
+int symnmf_spectral_probe(const float* S, int64_t n, int64_t lds, int32_t p, int32_t max_iters,
+                          double tol, uint64_t seed, double* eigvals_host, int32_t* iters_host,
+                          void* ws, size_t ws_bytes, void* hip_stream) {
+    if (!S || !eigvals_host || n < 1 || n > INT32_MAX / 2 || lds < n || lds % 4 ||
+        !aligned(S, 16) || p < 1 || max_iters < 1 || !(tol >= 0.0))
+        return SYMNMF_E_INVALID;
+    const int w = probe_width(p);
+    if (w > kMaxWidth || w > n) return SYMNMF_E_INVALID;
+    const size_t need = probe_layout(nullptr, n, p, nullptr);
+    if (!ws_ok(ws, ws_bytes, need)) return SYMNMF_E_WORKSPACE;
+    ProbeLayout L;
+    probe_layout(ws, n, p, &L);
+    hipStream_t st = as_stream(hip_stream);
+    const int nn = (int)n;
+    FullPlan fp = full_plan(nn);
+    const int ldp = ldp_of(w);
+    const int nblk = crossgram_blocks(nn);
+
+    float* Q = L.Q;
+    float* Y = L.Y;
+    HIPCHK(launch_init_uniform(Y, (int64_t)n * w, 2.f, -1.f, seed, st));
+    int rc = orthonormalize(Y, Q, nn, w, L, st);
+    if (rc != SYMNMF_OK) return rc;
+
+    std::vector<double> T((size_t)w * w), ev, prev, theta;
+    int it = 0;
+    bool converged = false;
+    for (it = 1; it <= max_iters; ++it) {
+        {
+            ProfScope ps(SYMNMF_PROF_SH_PROBE, 4.0 * n * (double)n + 8.0 * n * w, st);
+            HIPCHK(launch_sh_panel(S, lds, Q, nullptr, w, fp.rp, fp.nsplit, L.part, ldp, st));
+        }
+        HIPCHK(launch_reduce_partials(L.part, fp.nsplit, nn, w, ldp, Y, nullptr, nullptr, st));
+        HIPCHK(launch_crossgram(Q, Y, nn, w, L.cg_part, nblk, L.C, st));
+        HIPCHK(hipMemcpyAsync(T.data(), L.C, sizeof(double) * w * w, hipMemcpyDeviceToHost, st));
+        HIPCHK(hipStreamSynchronize(st));
+        for (int i = 0; i < w; ++i)
+            for (int j = i + 1; j < w; ++j) {
+                const double s = 0.5 * (T[(size_t)i * w + j] + T[(size_t)j * w + i]);
+                T[(size_t)i * w + j] = T[(size_t)j * w + i] = s;
+            }
+        for (double v : T)
+            if (!std::isfinite(v)) return SYMNMF_E_NONFINITE;
+        std::vector<double> A = T;
+        jacobi_eig(w, A, ev, nullptr);
+        std::vector<int> order(w);
+        for (int i = 0; i < w; ++i) order[i] = i;
+        std::stable_sort(order.begin(), order.end(),
+                         [&](int a, int b) { return std::fabs(ev[a]) > std::fabs(ev[b]); });
+        theta.assign(p, 0.0);
+        for (int i = 0; i < p; ++i) theta[i] = ev[order[i]];
+        if (!prev.empty()) {
+            double mx = 0.0;
+            for (int i = 0; i < p; ++i) mx = std::max(mx, std::fabs(theta[i] - prev[i]));
+            if (mx <= tol * std::fabs(theta[0])) {
+                converged = true;
+                break;
+            }
+        }
+        prev = theta;
+        if (it == max_iters) break;
+        rc = orthonormalize(Y, Q, nn, w, L, st);
+        if (rc != SYMNMF_OK) return rc;
+    }
+    for (int i = 0; i < p; ++i) eigvals_host[i] = theta[i];
+    if (iters_host) *iters_host = std::min(it, (int)max_iters);
+    return converged ? SYMNMF_OK : SYMNMF_W_NOT_CONVERGED;
+}
+
+// ---------------------------------------------------------------------------
+namespace {
+
+// gamma_{k+1} = lambda_{k+1} / |lambda_{k+2}| (1-based, descending |lambda|),
+// denominator floored at 1e-6 |lambda_1| (P1 "Why this solver").
+double gap_ratio(const double* ev, int k) {
+    const double lam1 = std::fabs(ev[0]);
+    double den = std::fabs(ev[k + 1]);
+    if (den <= 1e-6 * lam1) den = 1e-6 * lam1;
+    return ev[k] / den;
+}
+
+// |B|0 from gamma: 2^floor(log2(max(1, gamma/threshold nb))), capped at nb.
+int initial_blocks(double gamma, int nb, double threshold) {
+    if (gamma >= threshold) return nb;
+    const double x = std::max(1.0, gamma / threshold * (double)nb);
+    int e = (int)std::floor(std::log2(x));
+    int64_t v = (int64_t)1 << std::min(e, 30);
+    return (int)std::min<int64_t>(nb, v);
+}
+
+// Fisher-Yates over [0, nb) keyed by (seed, t); the first nsel slots, sorted.
+void sample_blocks(uint64_t seed, int t, int nb, int nsel, std::vector<int>& perm, int* out) {
+    perm.resize(nb);
+    for (int i = 0; i < nb; ++i) perm[i] = i;
+    const uint64_t key = seed ^ kSamplerKeyXor;
+    for (int j = 0; j < nsel; ++j) {
+        const uint64_t r = splitmix64(key, ((uint64_t)(uint32_t)t << 32) + (uint64_t)j);
+        const int pick = j + (int)(r % (uint64_t)(nb - j));
+        std::swap(perm[j], perm[pick]);
+    }
+    std::sort(perm.begin(), perm.begin() + nsel);
+    for (int j = 0; j < nsel; ++j) out[j] = perm[j];
+}
+
+}  // namespace
+
+int symnmf_fit(const float* S, int64_t n, int64_t lds, int32_t k, const symnmf_fit_params* prm,
+               const double* eigvals_host, int32_t n_eig, float* H, float* G,
+               double* obj_trace_host, int32_t obj_trace_cap, symnmf_fit_report* rep_host,
+               void* ws, size_t ws_bytes, void* hip_stream) {
+    const auto t_start = std::chrono::steady_clock::now();
+    symnmf_fit_params P;
+    if (prm) P = *prm; else symnmf_fit_params_default(&P);
+    if (!S || !H || n < 1 || n > INT32_MAX / 2 || k < 1 || k > kMaxK || k > n || lds < n ||
+        lds % 4 || !aligned(S, 16) || !aligned(H, 4))
+        return SYMNMF_E_INVALID;
+    if (P.solver < 0 || P.solver > 2 || P.max_iters < 0 || !(P.eps > 0.0) || P.block_rows < 4 ||
+        !(P.tol_rel >= 0.0) || !(P.stall_tol >= 0.0) || P.init < 0 || P.init > 2 ||
+        !(P.gap_threshold > 0.0) || (P.resume && !G) || (obj_trace_cap > 0 && !obj_trace_host) ||
+        obj_trace_cap < 0 || !std::isfinite(P.lr) || !std::isfinite(P.phi0))
+        return SYMNMF_E_INVALID;
+    if (P.init == SYMNMF_INIT_UNIFORM && !(P.init_scale > 0.0)) return SYMNMF_E_INVALID;
+    const int nb = (int)cdiv(n, P.block_rows);
+    const bool need_eig = P.solver != SYMNMF_FULL && !(P.phi0 > 0.0) && nb > 1;
+    if (need_eig && (!eigvals_host || n_eig < k + 2)) return SYMNMF_E_INVALID;
+    const size_t need = fit_layout(nullptr, n, k, P.max_iters, P.block_rows, nullptr);
+    if (!ws_ok(ws, ws_bytes, need)) return SYMNMF_E_WORKSPACE;
+    FitLayout L;
+    fit_layout(ws, n, k, P.max_iters, P.block_rows, &L);
+    hipStream_t st = as_stream(hip_stream);
+    const int nn = (int)n;
+    const int64_t nk = (int64_t)n * k;
+    const int ldp = ldp_of(k);
+    const int nblk = (int)cdiv(n, kUpdRows);
+
+    // ---- ||S||^2 and mean(S) (one pass over S)
+    HIPCHK(launch_s_stats(S, lds, nn, L.stats_part, st));
+    HIPCHK(launch_s_stats_final(L.stats_part, (int)cdiv(n, 64), L.stats_out, st));
+    double stats[2];
+    HIPCHK(hipMemcpyAsync(stats, L.stats_out, sizeof(stats), hipMemcpyDeviceToHost, st));
+    HIPCHK(hipStreamSynchronize(st));
+    const double S_sum = stats[0], S_fro2 = stats[1];
+    if (!std::isfinite(S_sum) || !std::isfinite(S_fro2)) return SYMNMF_E_NONFINITE;
+    const double S_mean = S_sum / ((double)n * (double)n);
+
+    // ---- readings for the undefined scale-matched init and default lr
+    const double a_sm = 2.0 * std::sqrt(std::max(0.0, S_mean) / k);
+    const double lr = P.lr > 0.0 ? P.lr : std::sqrt(std::max(0.0, S_mean) / k);
+    double init_scale = std::nan("");
+    if (P.init == SYMNMF_INIT_CALLER) {
+        HIPCHK(launch_copy(L.Hb[0], H, nk, st));
+    } else {
+        init_scale = P.init == SYMNMF_INIT_UNIFORM ? P.init_scale : a_sm;
+        HIPCHK(launch_init_uniform(L.Hb[0], nk, (float)init_scale, 0.f, P.seed, st));
+    }
+    if (P.resume) HIPCHK(launch_copy(L.Gb[0], G, nk, st));
+    else HIPCHK(launch_fill(L.Gb[0], nk, 0.f, st));
+
+    // ---- device state
+    {
+        FitDev h;
+        std::memset(&h, 0, sizeof(h));
+        h.S_fro2 = S_fro2;
+        h.tol = P.tol_rel;
+        HIPCHK(hipMemcpyAsync(L.fd, &h, sizeof(FitDev), hipMemcpyHostToDevice, st));
+        HIPCHK(hipStreamSynchronize(st));
+    }
+    // K_0 = H_0^T H_0
+    {
+        UpdateArgs a{};
+        a.n = nn; a.k = k; a.ldp = ldp; a.H = L.Hb[0]; a.fd = L.fd; a.gram_part = L.gram_part;
+        a.gram_only = 1;
+        HIPCHK(launch_update(a, st));
+        HIPCHK(launch_finalize(L.fd, nullptr, 0, nblk, k, nullptr, L.gram_part, 4 | 8, st));
+    }
+
+    // ---- branch choice (P1 "Why this solver"; P2 sketch)
+    double gamma = std::nan("");
+    int nsel = nb;
+    if (P.solver == SYMNMF_FULL || nb <= 1) {
+        nsel = nb;
+    } else if (P.phi0 > 0.0) {
+        nsel = (int)std::min<int64_t>(nb, std::max<int64_t>(1, (int64_t)std::ceil(P.phi0 * nb - 1e-12)));
+    } else {
+        gamma = gap_ratio(eigvals_host, k);
+        nsel = initial_blocks(gamma, nb, P.gap_threshold);
+    }
+    bool full = nsel >= nb;
+    const int start_branch = full ? 0 : 1;
+
+    const FullPlan fpl = full_plan(nn);
+    const double sh_bytes = 4.0 * n * (double)n + 8.0 * (double)nk;
+    int cur = 0, t = 0, doublings = 0, anchors = 0, last_exact = -1;
+    double f_anchor_prev = std::nan("");
+    bool have_anchor_prev = false;
+    FitDev hd;
+    std::vector<int> perm, lists;
+
+    auto exact_step = [&](bool write_anchor, int flags) -> int {
+        {
+            ProfScope ps(SYMNMF_PROF_SH_FULL, sh_bytes, st);
+            HIPCHK(launch_sh_panel(S, lds, L.Hb[cur], nullptr, k, fpl.rp, fpl.nsplit, L.part, ldp, st));
+        }
+        UpdateArgs a{};
+        a.n = nn; a.k = k; a.ldp = ldp; a.part = L.part; a.nsplit = fpl.nsplit;
+        a.pstride = (int64_t)n * ldp; a.H = L.Hb[cur]; a.G = L.Gb[cur];
+        a.Hn = L.Hb[cur ^ 1]; a.Gn = L.Gb[cur ^ 1];
+        a.Ha = write_anchor ? L.Ha : nullptr; a.Pa = write_anchor ? L.Pa : nullptr;
+        a.fd = L.fd; a.lr = (float)lr; a.eps = (float)P.eps;
+        a.tr_part = L.tr_part; a.gram_part = L.gram_part;
+        {
+            ProfScope ps(SYMNMF_PROF_UPDATE, (double)nk * 4.0 * (5 + fpl.nsplit), st);
+            HIPCHK(launch_update(a, st));
+        }
+        HIPCHK(launch_finalize(L.fd, L.f_trace, t, nblk, k, L.tr_part, L.gram_part, flags, st));
+        cur ^= 1;
+        ++t;
+        return SYMNMF_OK;
+    };
+    auto sampled_step = [&](const int* blocks_dev) -> int {
+        const FullPlan sp = sampled_plan(nn, blocks_dev, nsel, P.block_rows);
+        {
+            const double rows = std::min<double>((double)nsel * P.block_rows, (double)n);
+            ProfScope ps(SYMNMF_PROF_SH_SAMPLED, 4.0 * rows * (double)n + 8.0 * (double)nk, st);
+            HIPCHK(launch_sh_panel(S, lds, L.Hb[cur], L.Ha, k, sp.rp, sp.nsplit, L.part, ldp, st));
+        }
+        UpdateArgs a{};
+        a.n = nn; a.k = k; a.ldp = ldp; a.part = L.part; a.nsplit = sp.nsplit;
+        a.pstride = (int64_t)n * ldp; a.Pt = L.Pa; a.pscale = (float)((double)nb / nsel);
+        a.H = L.Hb[cur]; a.G = L.Gb[cur]; a.Hn = L.Hb[cur ^ 1]; a.Gn = L.Gb[cur ^ 1];
+        a.fd = L.fd; a.lr = (float)lr; a.eps = (float)P.eps; a.gram_part = L.gram_part;
+        {
+            ProfScope ps(SYMNMF_PROF_UPDATE, (double)nk * 4.0 * (6 + sp.nsplit), st);
+            HIPCHK(launch_update(a, st));
+        }
+        HIPCHK(launch_finalize(L.fd, L.f_trace, t, nblk, k, nullptr, L.gram_part, 4, st));
+        cur ^= 1;
+        ++t;
+        return SYMNMF_OK;
+    };
+    auto read_state = [&]() -> int {
+        HIPCHK(hipMemcpyAsync(&hd, L.fd, offsetof(FitDev, Kd), hipMemcpyDeviceToHost, st));
+        HIPCHK(hipStreamSynchronize(st));
+        return SYMNMF_OK;
+    };
+
+    int rc = SYMNMF_OK;
+    bool stopped = false;  // device stop flag seen
+    int cur_at_stop = 0;
+    // ---- Block-SVRG branch (P1 "Factorizing with SymNMF": SVRG-corrected
+    // block-sampled gradient, sample grown toward the full gradient when
+    // progress stalls)
+    while (!full && t < P.max_iters) {
+        rc = exact_step(true, 1 | 4);
+        if (rc) return rc;
+        ++anchors;
+        last_exact = t - 1;
+        if ((rc = read_state())) return rc;
+        if (hd.status == -4) return SYMNMF_E_NONFINITE;
+        const double f = hd.f_prev;
+        if (have_anchor_prev && (f_anchor_prev - f) < P.stall_tol * f_anchor_prev) {
+            nsel = std::min(2 * nsel, nb);
+            ++doublings;
+            if (nsel >= nb) full = true;
+        }
+        f_anchor_prev = f;
+        have_anchor_prev = true;
+        if (full) break;
+        const int E = (int)cdiv(nb, nsel);
+        const int steps = std::min(E - 1, P.max_iters - t);
+        if (steps <= 0) continue;
+        lists.assign((size_t)steps * nsel, 0);
+        for (int s = 0; s < steps; ++s) sample_blocks(P.seed, t + s, nb, nsel, perm, &lists[(size_t)s * nsel]);
+        HIPCHK(hipMemcpyAsync(L.blocks, lists.data(), sizeof(int) * lists.size(), hipMemcpyHostToDevice, st));
+        HIPCHK(hipStreamSynchronize(st));
+        for (int s = 0; s < steps; ++s) {
+            rc = sampled_step(L.blocks + (size_t)s * nsel);
+            if (rc) return rc;
+        }
+    }
+    // ---- full-batch branch (P2 sketch: g = 4 (H (H^T H) - S H))
+    if (full) {
+        const int t0 = t, cur0 = cur;
+        const int every = std::max(1, P.check_every);
+        while (t < P.max_iters) {
+            const int batch = std::min(every, P.max_iters - t);
+            for (int b = 0; b < batch; ++b) {
+                rc = exact_step(false, 1 | 2 | 4);
+                if (rc) return rc;
+            }
+            if ((rc = read_state())) return rc;
+            if (hd.done) {
+                stopped = true;
+                break;
+            }
+        }
+        if (stopped) {
+            if (hd.status == -4) return SYMNMF_E_NONFINITE;
+            t = hd.stop_iter;
+            cur_at_stop = (cur0 + (t - t0)) & 1;
+            cur = cur_at_stop;
+            last_exact = t;
+        } else if (t > t0) {
+            last_exact = t - 1;
+        }
+    } else if ((rc = read_state())) {
+        return rc;
+    }
+    const bool converged = stopped && hd.status == 1;
+    const int iters = t;
+
+    // ---- outputs
+    HIPCHK(launch_copy(H, L.Hb[cur], nk, st));
+    if (G) HIPCHK(launch_copy(G, L.Gb[cur], nk, st));
+    HIPCHK(launch_fill(reinterpret_cast<float*>(L.zero_rows), 1, 0.f, st));
+    HIPCHK(launch_count_zero_rows(L.Hb[cur], nn, k, L.zero_rows, st));
+    int zero_rows = 0;
+    HIPCHK(hipMemcpyAsync(&zero_rows, L.zero_rows, sizeof(int), hipMemcpyDeviceToHost, st));
+    const int evaluated = converged ? iters + 1 : iters;
+    const int ncopy = std::min(obj_trace_cap, evaluated);
+    if (ncopy > 0)
+        HIPCHK(hipMemcpyAsync(obj_trace_host, L.f_trace, sizeof(double) * ncopy, hipMemcpyDeviceToHost, st));
+    double f_last = std::nan("");
+    if (last_exact >= 0)
+        HIPCHK(hipMemcpyAsync(&f_last, L.f_trace + last_exact, sizeof(double), hipMemcpyDeviceToHost, st));
+    HIPCHK(hipStreamSynchronize(st));
+
+    if (rep_host) {
+        symnmf_fit_report& r = *rep_host;
+        std::memset(&r, 0, sizeof(r));
+        r.iterations = iters;
+        r.converged = converged ? 1 : 0;
+        r.start_branch = start_branch;
+        r.final_branch = full ? 0 : 1;
+        r.blocks_final = nsel;
+        r.n_blocks = nb;
+        r.doublings = doublings;
+        r.zero_rows = zero_rows;
+        r.f_last_iter = last_exact;
+        r.anchors = anchors;
+        r.gamma = gamma;
+        r.lr_used = lr;
+        r.init_scale_used = init_scale;
+        r.f_last = f_last;
+        r.S_fro2 = S_fro2;
+        r.S_mean = S_mean;
+        r.seconds = std::chrono::duration<double>(std::chrono::steady_clock::now() - t_start).count();
+    }
+    if (converged || P.tol_rel == 0.0) return SYMNMF_OK;
+    return SYMNMF_W_NOT_CONVERGED;
+}
+
+}  // extern "C"

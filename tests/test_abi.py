@@ -1,0 +1,166 @@
+"""C-ABI checks that need no GPU: the library loads, exports every function
+include/symnmf.h declares, reports its defaults, sizes workspaces as O(n k),
+and rejects invalid arguments before any device work (no compute calls)."""
+import ctypes
+import json
+import os
+import re
+
+import pytest
+
+from symmetric_nmf_clustering_amd import _lib as L
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "symnmf.h")
+
+pytestmark = pytest.mark.skipif(not os.path.exists(L.LIB_PATH),
+                                reason="libsymnmf.so not built (run __graft_entry__.build())")
+
+
+def header_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    names = re.findall(r"\b(symnmf_[A-Za-z0-9_]+)\s*\(", text)
+    return sorted(set(names))
+
+
+def test_header_declares_the_boundary():
+    names = header_functions()
+    for n in ("symnmf_build_S", "symnmf_spectral_probe", "symnmf_fit", "symnmf_labels"):
+        assert n in names
+
+
+def test_every_declared_symbol_is_exported():
+    lib = L.load()
+    for name in header_functions():
+        assert hasattr(lib, name), name
+    assert {n for n, _, _ in L.SIGNATURES} == set(header_functions())
+
+
+def test_abi_version_and_status_strings():
+    lib = L.load()
+    assert lib.symnmf_abi_version() == 1
+    for s in (0, 1, -1, -2, -3, -4, -5):
+        assert len(L.status_string(s)) > 0
+    assert L.status_string(12345) == "unknown status"
+
+
+def test_defaults_are_the_pages(golden_dir):
+    c = json.load(open(os.path.join(golden_dir, "page_constants.json")))
+    lib = L.load()
+    p = L.FitParams()
+    lib.symnmf_fit_params_default(ctypes.byref(p))
+    assert p.eps == c["eps"]["value"]
+    assert p.max_iters == c["steps"]["value"]
+    assert p.gap_threshold == c["gap_threshold"]["value"]
+    assert p.solver == L.AUTO and p.block_rows == 1024 and p.tol_rel == 1e-6
+
+
+def test_struct_layout_matches_the_c_compiler(tmp_path):
+    # compile a probe against the header with gcc and compare every field offset
+    import shutil
+    import subprocess
+    cc = shutil.which("gcc") or shutil.which("cc")
+    if cc is None:
+        pytest.skip("no C compiler")
+    lines = ['#include <stdio.h>', '#include <stddef.h>', '#include "symnmf.h"', 'int main(void) {']
+    for cname, cls in (("symnmf_fit_params", L.FitParams), ("symnmf_fit_report", L.FitReport)):
+        lines.append(f'printf("{cname} size %zu\\n", sizeof({cname}));')
+        for f, _ in cls._fields_:
+            lines.append(f'printf("{cname} {f} %zu\\n", offsetof({cname}, {f}));')
+    lines += ["return 0;", "}"]
+    src = tmp_path / "probe.c"
+    src.write_text("\n".join(lines))
+    exe = tmp_path / "probe"
+    subprocess.run([cc, "-I", os.path.join(ROOT, "include"), str(src), "-o", str(exe)], check=True)
+    out = subprocess.run([str(exe)], check=True, capture_output=True, text=True).stdout.split("\n")
+    got = {(a, b): int(c) for a, b, c in (l.split() for l in out if l.strip())}
+    for cname, cls in (("symnmf_fit_params", L.FitParams), ("symnmf_fit_report", L.FitReport)):
+        assert got[(cname, "size")] == ctypes.sizeof(cls)
+        for f, _ in cls._fields_:
+            assert got[(cname, f)] == getattr(cls, f).offset, (cname, f)
+
+
+def test_workspace_is_order_nk(golden_dir):
+    lib = L.load()
+    c = json.load(open(os.path.join(golden_dir, "page_constants.json")))
+    k = 24
+    for n in (1000, 100000, 1000000):
+        fit = lib.symnmf_workspace_bytes(L.OP_FIT, n, k, 0, None)
+        assert 0 < fit < 64 * n * k * 4 + 2 ** 20
+        sh = lib.symnmf_workspace_bytes(L.OP_SH, n, k, 0, None)
+        assert 0 < sh < 20 * n * k * 4 + 2 ** 20
+        probe = lib.symnmf_workspace_bytes(L.OP_PROBE, n, 64, 0, None)
+        assert 0 < probe < 20 * n * 80 * 4 + 2 ** 22
+    # peak device storage of a fit at n = 1e5: the S itself (4 n^2) plus
+    # workspace well under 1% of it (the pages' ~4 n^2 bytes)
+    n = 100000
+    total = 4 * n * n + lib.symnmf_workspace_bytes(L.OP_FIT, n, k, 0, None)
+    assert total / (n * n) < c["peak_storage_bytes_per_n2"]["trace_formulation"] * 1.01
+    assert lib.symnmf_workspace_bytes(L.OP_FIT, n, 65, 0, None) == 0  # k > 64
+    assert lib.symnmf_workspace_bytes(L.OP_PROBE, n, 113, 0, None) == 0  # w > 128
+    assert lib.symnmf_workspace_bytes(L.OP_BUILD_S, n, 1, 1, None) == 0  # T < 2
+    assert lib.symnmf_workspace_bytes(99, n, 1, 1, None) == 0
+
+
+FAKE = ctypes.c_void_p(0x10000)  # never dereferenced: every call below fails validation
+
+
+def test_invalid_arguments_rejected_before_device_work():
+    lib = L.load()
+    z = ctypes.c_size_t(1 << 30)
+    # null pointers / bad sizes / bad layouts
+    assert lib.symnmf_build_S(0, None, 10, 10, 10, 0.05, FAKE, 12, None, FAKE, z, None) == L.E_INVALID
+    assert lib.symnmf_build_S(0, FAKE, 1, 10, 10, 0.05, FAKE, 12, None, FAKE, z, None) == L.E_INVALID
+    assert lib.symnmf_build_S(0, FAKE, 10, 10, 10, 0.05, FAKE, 10, None, FAKE, z, None) == L.E_INVALID  # lds % 4
+    assert lib.symnmf_build_S(1, FAKE, 10, 10, 10, 0.0, FAKE, 12, None, FAKE, z, None) == L.E_INVALID   # tail_frac
+    assert lib.symnmf_build_S(7, FAKE, 10, 10, 10, 0.05, FAKE, 12, None, FAKE, z, None) == L.E_INVALID  # kind
+    assert lib.symnmf_build_S(0, FAKE, 10, 10, 10, 0.05, FAKE, 12, None, None, z, None) == L.E_WORKSPACE
+    assert lib.symnmf_build_S(0, FAKE, 10, 10, 10, 0.05, FAKE, 12, None, FAKE, 8, None) == L.E_WORKSPACE
+    ev = (ctypes.c_double * 8)()
+    assert lib.symnmf_spectral_probe(FAKE, 100, 100, 0, 10, 1e-6, 0, ev, None, FAKE, z, None) == L.E_INVALID
+    assert lib.symnmf_spectral_probe(FAKE, 20, 20, 8, 10, 1e-6, 0, ev, None, FAKE, z, None) == L.E_INVALID  # w > n
+    assert lib.symnmf_spectral_probe(FAKE, 100, 100, 8, 10, 1e-6, 0, ev, None, FAKE, 64, None) == L.E_WORKSPACE
+    P = FAKE
+    assert lib.symnmf_sh(FAKE, 100, 100, FAKE, 0, P, None, FAKE, z, None) == L.E_INVALID
+    assert lib.symnmf_sh(FAKE, 100, 100, FAKE, 129, P, None, FAKE, z, None) == L.E_INVALID
+    assert lib.symnmf_sh(FAKE, 100, 98, FAKE, 8, P, None, FAKE, z, None) == L.E_INVALID
+    assert lib.symnmf_labels(None, 10, 3, FAKE, None) == L.E_INVALID
+    assert lib.symnmf_labels(FAKE, 0, 3, FAKE, None) == L.OK  # empty input: nothing to do
+
+
+def test_fit_argument_validation():
+    lib = L.load()
+    z = ctypes.c_size_t(1 << 40)
+    rep = L.FitReport()
+
+    def call(params, n=100, lds=100, k=4, eig=None, n_eig=0, H=FAKE, G=None, ws=FAKE, wsb=z):
+        return lib.symnmf_fit(FAKE, n, lds, k, ctypes.byref(params), eig, n_eig, H, G, None, 0,
+                              ctypes.byref(rep), ws, wsb, None)
+
+    def P(**kw):
+        p = L.FitParams()
+        lib.symnmf_fit_params_default(ctypes.byref(p))
+        for a, b in kw.items():
+            setattr(p, a, b)
+        return p
+
+    full = dict(solver=L.FULL)
+    assert call(P(**full), k=0) == L.E_INVALID
+    assert call(P(**full), k=65) == L.E_INVALID
+    assert call(P(**full), n=3, lds=4, k=4) == L.E_INVALID          # k > n
+    assert call(P(**full), lds=98) == L.E_INVALID                   # lds < n
+    assert call(P(**full), lds=102) == L.E_INVALID                  # lds % 4
+    assert call(P(**full), H=None) == L.E_INVALID
+    assert call(P(eps=0.0, **full)) == L.E_INVALID
+    assert call(P(max_iters=-1, **full)) == L.E_INVALID
+    assert call(P(resume=1, **full)) == L.E_INVALID                 # resume needs G
+    assert call(P(init=L.INIT_UNIFORM, init_scale=0.0, **full)) == L.E_INVALID
+    assert call(P(solver=9)) == L.E_INVALID
+    # AUTO with several blocks needs eigenvalues (>= k + 2) unless phi0 > 0
+    assert call(P(block_rows=10)) == L.E_INVALID
+    ev = (ctypes.c_double * 5)(10, 9, 8, 7, 6)
+    assert call(P(block_rows=10), eig=ev, n_eig=5) == L.E_INVALID   # needs 6
+    assert call(P(**full), ws=None) == L.E_WORKSPACE
+    assert call(P(**full), wsb=ctypes.c_size_t(1024)) == L.E_WORKSPACE
+    assert call(P(**full), ws=ctypes.c_void_p(0x10010)) == L.E_WORKSPACE  # misaligned
