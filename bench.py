@@ -1,0 +1,222 @@
+#!/usr/bin/env python3
+"""Benchmark of the SymNMF clustering hot path on one MI355X.
+
+One timed step is one whole job on one synthetic returns window resident in
+HBM: build |corr| S (n x n fp32) with the MFMA Gram, run the spectral probe
+(top 64 eigenvalues), fit S ~ H H^T with the AdaptGrow-selected solver to
+convergence, and take the argmax labels. ``value`` is the number of SymNMF
+iterations completed per second of whole-job time. The S.H kernel's achieved
+HBM bandwidth is measured live with HIP events on the launch stream (the
+library's kernel timing) over the timed region.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
+FP32_MFMA_PEAK_TFLOPS = 157.3  # MI355X dense fp32 matrix
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=3)
+    ap.add_argument("--warmup", type=int, default=1)
+    ap.add_argument("--workload", default="tfactor_n100000_k24")
+    ap.add_argument("--solver", default="auto", choices=["auto", "full", "block_svrg"])
+    ap.add_argument("--probe-p", type=int, default=64)
+    ap.add_argument("--probe-iters", type=int, default=300)
+    ap.add_argument("--max-iters", type=int, default=2000)
+    ap.add_argument("--full-iters", type=int, default=40,
+                    help="full-batch steps timed after the jobs (reported separately)")
+    ap.add_argument("--cpu-rows", type=int, default=4096,
+                    help="rows of S.H the CPU oracle computes for its baseline sample")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    return ap.parse_args()
+
+
+def cpu_baseline(w, k, rows):
+    """The CPU oracle timed on a bounded sample of one full-batch iteration:
+    the S.H product on `rows` rows of S (the oracle builds those rows itself,
+    untimed) plus the gradient and AdaGrad update on all n x k entries; scaled
+    to iterations per second of the whole n x n problem."""
+    import numpy as np
+
+    import oracle
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([d.get("num_threads", 1) for d in threadpool_info()] + [1])
+    except Exception:  # pragma: no cover - threadpoolctl missing
+        cores = os.cpu_count() or 1
+    n = w.n
+    rows = min(rows, n)
+    S_rows = oracle.abs_corr_rows(w.X, np.arange(rows))
+    mean_est = float(S_rows.mean())
+    H = oracle.init_uniform(n, k, oracle.init_scale_matched(mean_est, k), 0)
+    lr = oracle.default_lr(mean_est, k)
+    reps = 3
+    t0 = time.perf_counter()
+    for _ in range(reps):
+        P_rows, _ = oracle.sh_product(S_rows, H)
+    t_sh = (time.perf_counter() - t0) / reps
+    P = np.zeros((n, k))
+    P[:rows] = P_rows
+    G = np.zeros_like(H)
+    t0 = time.perf_counter()
+    for _ in range(reps):
+        K = H.T @ H
+        g = 4.0 * (H @ K - P)
+        Hn, Gn = oracle.adagrad_step(H, G, g, lr)
+        _ = float((H * P).sum()) + float((K * K).sum())
+    t_rest = (time.perf_counter() - t0) / reps
+    per_iter = t_sh * (n / rows) + t_rest
+    return {"value": 1.0 / per_iter, "unit": "iters/s", "cores": int(cores), "kind": "oracle",
+            "sample": (f"S.H on {rows} of {n} rows (fp64 numpy matmul, x{n / rows:.1f}) plus the "
+                       f"full n x k gradient/AdaGrad update; {reps} repetitions each"),
+            "seconds_per_iter": per_iter}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this build runs on exactly one GPU; --gpus must be 1",
+                          "n_gpus": args.gpus}))
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    from symmetric_nmf_clustering_amd import _lib, api, metrics, synth
+
+    torch.cuda.set_device(0)
+    dev = torch.device("cuda", 0)
+    w = synth.workload(args.workload)
+    n, k, T = w.n, w.k, w.T
+    X = torch.from_numpy(w.X).to(dev)
+    S = api.alloc_S(n, dev)
+
+    def job():
+        ph = {}
+        torch.cuda.synchronize()
+        t = time.perf_counter()
+        _, fro = api.build_S(X, "abscorr", out=S)
+        torch.cuda.synchronize()
+        ph["build_ms"] = (time.perf_counter() - t) * 1e3
+        t = time.perf_counter()
+        ev, pits, pconv = api.spectral_probe(S, p=args.probe_p, max_iters=args.probe_iters,
+                                             tol=1e-6, seed=0)
+        ph["probe_ms"] = (time.perf_counter() - t) * 1e3
+        ph["probe_iters"] = pits
+        ph["probe_converged"] = bool(pconv)
+        t = time.perf_counter()
+        res = api.fit(S, k, solver=args.solver, eigvals=ev, max_iters=args.max_iters,
+                      tol_rel=1e-6, seed=0)
+        torch.cuda.synchronize()
+        ph["fit_s"] = time.perf_counter() - t
+        t = time.perf_counter()
+        lab = api.labels(res.H)
+        torch.cuda.synchronize()
+        ph["labels_ms"] = (time.perf_counter() - t) * 1e3
+        print(f"[bench] job: build {ph['build_ms']:.1f} ms, probe {ph['probe_ms']:.0f} ms "
+              f"({pits} it), fit {ph['fit_s']:.2f} s ({res.report['iterations']} it, "
+              f"converged={res.report['converged']}), labels {ph['labels_ms']:.2f} ms",
+              file=sys.stderr, flush=True)
+        return res, lab, ev, ph, fro
+
+    for _ in range(args.warmup):
+        job()
+
+    api.profile_reset()
+    api.profile_enable(True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    iters = 0
+    phases = []
+    for _ in range(args.steps):
+        res, lab, ev, ph, fro = job()
+        iters += res.report["iterations"]
+        phases.append(ph)
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    api.profile_enable(False)
+    prof = {_lib.PROF_NAMES[i]: api.profile_read(i) for i in _lib.PROF_NAMES}
+
+    rep = res.report
+    ari = metrics.adjusted_rand_index(lab.cpu().numpy(), w.labels)
+
+    # full-batch rate on the same S (every step one S.H pass), reported beside
+    api.profile_reset()
+    api.profile_enable(True)
+    torch.cuda.synchronize()
+    tf = time.perf_counter()
+    full = api.fit(S, k, solver="full", max_iters=args.full_iters, tol_rel=0.0, seed=0)
+    torch.cuda.synchronize()
+    tf = time.perf_counter() - tf
+    api.profile_enable(False)
+    prof_full = api.profile_read(_lib.PROF_SH_FULL)
+
+    sh = prof["sh_full"] if prof["sh_full"]["launches"] else prof_full
+    sh_ms = sh["ms"] / max(1, sh["launches"])
+    sh_bytes = sh["bytes"] / max(1, sh["launches"])
+    achieved = sh_bytes / (sh_ms * 1e-3) / 1e9
+    kernels = {}
+    for name, d in list(prof.items()) + [("sh_full_fullbatch_run", prof_full)]:
+        if d["launches"]:
+            ms = d["ms"] / d["launches"]
+            kernels[name] = {"launches": d["launches"], "avg_ms": ms,
+                             "GBs": d["bytes"] / d["launches"] / (ms * 1e-3) / 1e9}
+
+    out = {
+        "metric": "SymNMF iters/sec + S·H HBM GB/s (% of peak) at n=100k, k=24, fp32",
+        "value": iters / elapsed,
+        "unit": "iters/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": elapsed / args.steps * 1e3,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": args.workload, "n": n, "k": k, "T": T, "S": "abscorr",
+                   "solver": args.solver, "probe_p": args.probe_p, "tol_rel": 1e-6,
+                   "parallelism": "single-gpu"},
+        "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": achieved / HBM_PEAK_GBS, "traffic": None,
+                     "kernel": "sh_panel_kernel (full S.H pass)", "avg_ms": sh_ms,
+                     "bytes_per_launch": sh_bytes},
+        "job": {"fit_iterations": rep["iterations"], "converged": bool(rep["converged"]),
+                "start_branch": "full" if rep["start_branch"] == 0 else "block_svrg",
+                "final_branch": "full" if rep["final_branch"] == 0 else "block_svrg",
+                "gamma_k1": rep["gamma"], "doublings": rep["doublings"],
+                "anchors": rep["anchors"], "f_last": rep["f_last"],
+                "time_to_convergence_s": float(np.median([p["fit_s"] for p in phases])),
+                "build_ms": float(np.median([p["build_ms"] for p in phases])),
+                "probe_ms": float(np.median([p["probe_ms"] for p in phases])),
+                "probe_iters": phases[-1]["probe_iters"],
+                "labels_ms": float(np.median([p["labels_ms"] for p in phases])),
+                "fit_iters_per_s": rep["iterations"] / float(np.median([p["fit_s"] for p in phases])),
+                "ari_vs_planted": ari, "lambda_top3": [float(x) for x in ev[:3]],
+                "lambda_k_k1_k2": [float(ev[k - 1]), float(ev[k]), float(ev[k + 1])]},
+        "full_batch": {"iters_per_s": args.full_iters / tf, "steps": args.full_iters},
+        "kernels": kernels,
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(w, k, args.cpu_rows)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -203,7 +203,8 @@ int symnmf_fit(const float* S, int64_t n, int64_t lds, int32_t k,
 
 /* Hard labels (P1 "Factorizing with SymNMF": the row-wise argmax of H):
  * labels[i] = argmax_c H[i, c], lowest index on ties; an all-zero row gets 0.
- * Asynchronous. Errors: E_INVALID, E_HIP. */
+ * n = 0 is a no-op (the pointers are not used). Asynchronous.
+ * Errors: E_INVALID, E_HIP. */
 int symnmf_labels(const float* H, int64_t n, int32_t k, int32_t* labels, void* hip_stream);
 
 const char* symnmf_status_string(int status);

@@ -66,12 +66,13 @@ hipError_t launch_s_stats_final(const double* part2, int nblk, double* out2, hip
 }
 
 // ---- element-wise helpers -------------------------------------------------------
-__global__ void init_uniform_kernel(float* __restrict__ H, int64_t count, float scale,
-                                    float shift, uint64_t seed) {
+// H[i] = scale * u(seed, i) + shift, formed in fp64 and rounded once to fp32.
+__global__ void init_uniform_kernel(float* __restrict__ H, int64_t count, double scale,
+                                    double shift, uint64_t seed) {
     const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-    if (i < count) H[i] = scale * uniform24(seed, (uint64_t)i) + shift;
+    if (i < count) H[i] = (float)(scale * (double)uniform24(seed, (uint64_t)i) + shift);
 }
-hipError_t launch_init_uniform(float* H, int64_t count, float scale, float shift, uint64_t seed,
+hipError_t launch_init_uniform(float* H, int64_t count, double scale, double shift, uint64_t seed,
                                hipStream_t st) {
     if (count <= 0) return hipSuccess;
     hipLaunchKernelGGL(init_uniform_kernel, dim3((unsigned)((count + 255) / 256)), dim3(256), 0,

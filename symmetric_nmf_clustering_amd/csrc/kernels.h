@@ -66,7 +66,7 @@ hipError_t launch_reduce_partials(const float* part, int nsplit, int n, int widt
 // ---- fit --------------------------------------------------------------------
 hipError_t launch_s_stats(const float* S, int64_t lds, int n, double* part2, hipStream_t st);
 hipError_t launch_s_stats_final(const double* part2, int nblk, double* out2, hipStream_t st);
-hipError_t launch_init_uniform(float* H, int64_t count, float scale, float shift, uint64_t seed,
+hipError_t launch_init_uniform(float* H, int64_t count, double scale, double shift, uint64_t seed,
                                hipStream_t st);
 hipError_t launch_fill(float* p, int64_t count, float v, hipStream_t st);
 hipError_t launch_copy(float* dst, const float* src, int64_t count, hipStream_t st);

@@ -419,8 +419,8 @@ int symnmf_profile_read(int which, int64_t* launches, double* total_ms, double* 
 
 // ---------------------------------------------------------------------------
 int symnmf_labels(const float* H, int64_t n, int32_t k, int32_t* labels, void* hip_stream) {
+    if (n == 0 && k >= 1) return SYMNMF_OK;  // empty input: nothing to do, pointers unused
     if (!H || !labels || n < 0 || k < 1 || n > INT32_MAX) return SYMNMF_E_INVALID;
-    if (n == 0) return SYMNMF_OK;
     HIPCHK(launch_labels(H, n, k, labels, as_stream(hip_stream)));
     return SYMNMF_OK;
 }
@@ -577,7 +577,7 @@ int symnmf_spectral_probe(const float* S, int64_t n, int64_t lds, int32_t p, int
 
     float* Q = L.Q;
     float* Y = L.Y;
-    HIPCHK(launch_init_uniform(Y, (int64_t)n * w, 2.f, -1.f, seed, st));
+    HIPCHK(launch_init_uniform(Y, (int64_t)n * w, 2.0, -1.0, seed, st));
     int rc = orthonormalize(Y, Q, nn, w, L, st);
     if (rc != SYMNMF_OK) return rc;
 
@@ -710,7 +710,7 @@ int symnmf_fit(const float* S, int64_t n, int64_t lds, int32_t k, const symnmf_f
         HIPCHK(launch_copy(L.Hb[0], H, nk, st));
     } else {
         init_scale = P.init == SYMNMF_INIT_UNIFORM ? P.init_scale : a_sm;
-        HIPCHK(launch_init_uniform(L.Hb[0], nk, (float)init_scale, 0.f, P.seed, st));
+        HIPCHK(launch_init_uniform(L.Hb[0], nk, init_scale, 0.0, P.seed, st));
     }
     if (P.resume) HIPCHK(launch_copy(L.Gb[0], G, nk, st));
     else HIPCHK(launch_fill(L.Gb[0], nk, 0.f, st));

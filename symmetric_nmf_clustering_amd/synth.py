@@ -72,7 +72,7 @@ def gaussian_blocks(n: int = 1024, k: int = 8, T: int = 256, a: float = 0.6,
     F = rng.standard_normal((T, k))
     E = rng.standard_normal((T, n))
     X = a * F[:, labels] + b * E
-    return Window(X.astype(np.float32), labels, k, "gaussian_blocks", seed,
+    return Window(np.ascontiguousarray(X, dtype=np.float32), labels, k, "gaussian_blocks", seed,
                   {"a": a, "b": b})
 
 
@@ -99,7 +99,7 @@ def student_factor(n: int = 8192, k: int = 24, T: int = 252, seed: int = 1,
     F = _t4_unit(rng, (T, k))
     E = _t4_unit(rng, (T, n))
     X = load * F[:, labels] + np.sqrt(1.0 - load * load) * E
-    return Window(X.astype(np.float32), labels, k, "student_factor", seed,
+    return Window(np.ascontiguousarray(X, dtype=np.float32), labels, k, "student_factor", seed,
                   {"sizes": sizes.tolist()})
 
 
@@ -125,7 +125,7 @@ def student_factor_stress(n: int = 8192, k: int = 24, T: int = 252,
     meta = dict(base.meta)
     meta.update({"stress_groups": groups.tolist(), "stress_day0": day0,
                  "stress_days": stress_days, "shock": shock})
-    return Window(X.astype(np.float32), base.labels, k,
+    return Window(np.ascontiguousarray(X, dtype=np.float32), base.labels, k,
                   "student_factor_stress", seed, meta)
 
 
