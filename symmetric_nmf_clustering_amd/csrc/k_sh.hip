@@ -4,21 +4,28 @@
 // Layout and mapping (gfx950, wave64, fp32 MFMA 16x16x4):
 //  * S is row-major and symmetric, so (S X)[i][c] = sum_j S[j][i] X[j][c]: the
 //    pass streams contiguous ROW panels of S and produces output columns.
-//  * A workgroup (4 waves) owns 256 consecutive columns i of S and one split
-//    (a set of rows j). Each lane loads one float4 of S per 4-row group:
-//    row j0 + (lane / 16), columns i0 + 4 (lane % 16) .. +3, so the four rows
-//    of a group are each read as 256 contiguous bytes per wave (1 KiB per
-//    workgroup).
-//  * Element q of the float4 feeds MFMA tile q as its B operand, so tile q
-//    owns output columns i0 + 4 n + q (n = 0..15); the A operand is X^T for 16
-//    columns of X (c-tile), taken straight from L1/L2 (X is small and reused by
-//    every column tile of a split).
-//  * Each output (i, c) accumulates one split's rows in fp32 (a few thousand
-//    terms at most), and splits are summed later in a fixed order, so the
-//    result is deterministic and its rounding error stays ~1e-6 relative.
-//  * Block b of the 1-D grid takes split b % nsplit and column tile
-//    b / nsplit; with nsplit a multiple of 8, every workgroup of a split lands
-//    on the same XCD, so that split's rows of X stay in one L2.
+//  * A workgroup (4 waves) owns 256 CW consecutive columns i of S and one
+//    split (a set of rows j). Per 4-row group each lane loads CW float4s of S:
+//    row j0 + (lane / 16), columns i0 + 64 w + 4 (lane % 16) .. +3, so every
+//    row of the group is read as 256 CW contiguous bytes per wave (1 KiB CW
+//    per workgroup).
+//  * Element q of a float4 feeds MFMA tile q as its B operand, so tile q owns
+//    output columns i0 + 4 n + q (n = 0..15); the A operand is X^T for 16
+//    columns of X (one c-tile), read straight from L1/L2 (X is small and
+//    shared by every column tile of a split).
+//  * Columns past the last full 16-column tile (4 or 8 of them, e.g. 16..23
+//    for k = 24) run as plain fp32 FMAs on the vector ALU instead of a padded
+//    MFMA tile: the matrix core and the vector ALU issue side by side, and no
+//    MFMA work is spent on padding. (fp32 MFMA is what keeps up with HBM at
+//    k = 24: the vector ALU alone, without packed fp32, would need ~90% of
+//    its issue slots.)
+//  * Each output (i, c) accumulates one split's rows in fp32 (n / 32 terms at
+//    most), and splits are summed later in a fixed order, so the result is
+//    deterministic and its rounding error stays ~1e-6 relative.
+//  * Block b of the 1-D grid takes column tile b % ntiles and split
+//    b / ntiles: the workgroups resident together sweep the same rows of S.
+#include <type_traits>
+
 #include "common.h"
 #include "kernels.h"
 
@@ -48,158 +55,271 @@ __device__ __forceinline__ bool split_segment(const RowPlan& rp, int s, int g, i
     return true;
 }
 
-template <int NC, bool DIFF>
+// NCM MFMA column tiles (16 columns each) plus NV <= 8 columns on the vector
+// ALU, CW float4 column groups per lane (64 CW columns per wave). XVEC: the
+// vector-ALU columns are read as float4s (row pitch a multiple of 4 and all
+// NV columns inside the width). SEG: a split may cover several row blocks
+// (kept out of the common single-range case, where the extra loop level
+// roughly doubles the register footprint).
+template <int NCM, int NV, int CW, bool DIFF, bool XVEC, bool SEG>
 __global__ __launch_bounds__(256) void sh_panel_kernel(const float* __restrict__ S, int64_t lds,
                                                        const float* __restrict__ X,
                                                        const float* __restrict__ Xa, int width,
                                                        RowPlan rp, int nsplit,
                                                        float* __restrict__ part, int ldp) {
-    const int split = blockIdx.x % nsplit;
-    const int tile = blockIdx.x / nsplit;
+    constexpr int U = 2;              // 4-row groups per main-loop trip
+    constexpr int WCOLS = 64 * CW;    // columns per wave
+    constexpr int NCM1 = NCM > 0 ? NCM : 1;
+    constexpr int NV1 = NV > 0 ? NV : 1;
+    const int n = rp.n;
+    const int ntiles = (n + 4 * WCOLS - 1) / (4 * WCOLS);
+    // column tile fastest: the workgroups running together sweep the same rows
+    const int tile = blockIdx.x % ntiles;
+    const int split = blockIdx.x / ntiles;
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
     const int r = lane >> 4;   // row of the 4-row group this lane loads
     const int cl = lane & 15;  // column quad / MFMA row index
-    const int n = rp.n;
-    const int col = tile * kShTileCols + wave * 64 + 4 * cl;
+    const int colbase = tile * (4 * WCOLS) + wave * WCOLS + 4 * cl;
+    const int c_v = 16 * NCM;  // first vector-ALU column
+    const bool tile_full = (tile + 1) * (4 * WCOLS) <= n;  // uniform over the workgroup
 
-    floatx4 acc[NC][4];
+    floatx4 macc[CW][NCM1][4];
+    float vacc[CW][4][NV1];
 #pragma unroll
-    for (int ct = 0; ct < NC; ++ct)
+    for (int w = 0; w < CW; ++w)
 #pragma unroll
-        for (int q = 0; q < 4; ++q) acc[ct][q] = floatx4{0.f, 0.f, 0.f, 0.f};
+        for (int q = 0; q < 4; ++q) {
+#pragma unroll
+            for (int ct = 0; ct < NCM; ++ct) macc[w][ct][q] = floatx4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int c = 0; c < NV; ++c) vacc[w][q][c] = 0.f;
+        }
 
-    const bool colok = col < n;
-    const bool colfull = col + 4 <= n;
-    const float* __restrict__ Sc = S + col;
+    // Loads are unconditional: an out-of-range column reads a clamped, valid
+    // address and the value is replaced by zero (edge tile only).
+    int scol[CW];
+#pragma unroll
+    for (int w = 0; w < CW; ++w) {
+        const int c0 = colbase + 64 * w;
+        scol[w] = c0 < n ? c0 : 0;
+    }
 
-    int jb, je;
-    for (int g = 0; split_segment(rp, split, g, jb, je); ++g) {
-    constexpr int U = 4;  // 4-row groups per main-loop trip (16 rows)
-    int j0 = jb;
-    for (; j0 + 4 * U <= je; j0 += 4 * U) {
-        float4 sv[U];
-        float av[U][NC];
+    // this lane's X values of row j: MFMA A operands and vector-ALU columns
+    auto load_x = [&](int64_t j, bool rowok, float (&a)[NCM1], float (&hv)[NV1]) {
+        const float* px = X + j * width;
+        const float* pxa = DIFF ? Xa + j * width : nullptr;
 #pragma unroll
-        for (int u = 0; u < U; ++u) {
-            const int j = j0 + 4 * u + r;
-            if (colok) {
-                sv[u] = *reinterpret_cast<const float4*>(Sc + (int64_t)j * lds);
-            } else {
-                sv[u] = float4{0.f, 0.f, 0.f, 0.f};
-            }
+        for (int ct = 0; ct < NCM; ++ct) {
+            const int c = 16 * ct + cl;
+            const bool ok = rowok && c < width;
+            const int off = c < width ? c : 0;
+            float v = px[off];
+            if (DIFF) v -= pxa[off];
+            a[ct] = ok ? v : 0.f;
+        }
+        if (NV > 0) {
+            if (XVEC) {
 #pragma unroll
-            for (int ct = 0; ct < NC; ++ct) {
-                const int c = 16 * ct + cl;
-                float v = 0.f;
-                if (c < width) {
-                    v = X[(int64_t)j * width + c];
-                    if (DIFF) v -= Xa[(int64_t)j * width + c];
+                for (int c4 = 0; c4 < NV; c4 += 4) {
+                    float4 v = *reinterpret_cast<const float4*>(px + c_v + c4);
+                    if (DIFF) {
+                        const float4 va = *reinterpret_cast<const float4*>(pxa + c_v + c4);
+                        v.x -= va.x;
+                        v.y -= va.y;
+                        v.z -= va.z;
+                        v.w -= va.w;
+                    }
+                    hv[c4 + 0] = rowok ? v.x : 0.f;
+                    hv[c4 + 1] = rowok ? v.y : 0.f;
+                    hv[c4 + 2] = rowok ? v.z : 0.f;
+                    hv[c4 + 3] = rowok ? v.w : 0.f;
                 }
-                av[u][ct] = v;
+            } else {
+#pragma unroll
+                for (int c = 0; c < NV; ++c) {
+                    const bool ok = rowok && c_v + c < width;
+                    const int off = c_v + c < width ? c_v + c : 0;
+                    float v = px[off];
+                    if (DIFF) v -= pxa[off];
+                    hv[c] = ok ? v : 0.f;
+                }
             }
         }
-        if (!colfull) {
+    };
+    auto load_s = [&](int64_t j, bool edge, float4 (&sv)[CW]) {
+        const float* ps = S + j * lds;
+#pragma unroll
+        for (int w = 0; w < CW; ++w) {
+            float4 v = *reinterpret_cast<const float4*>(ps + scol[w]);
+            if (edge) {
+                const int c0 = colbase + 64 * w;
+                v.x = c0 < n ? v.x : 0.f;
+                v.y = c0 + 1 < n ? v.y : 0.f;
+                v.z = c0 + 2 < n ? v.z : 0.f;
+                v.w = c0 + 3 < n ? v.w : 0.f;
+            }
+            sv[w] = v;
+        }
+    };
+    auto compute = [&](const float4 (&sv)[CW], const float (&a)[NCM1], const float (&hv)[NV1]) {
+#pragma unroll
+        for (int w = 0; w < CW; ++w) {
+            const float s4[4] = {sv[w].x, sv[w].y, sv[w].z, sv[w].w};
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+#pragma unroll
+                for (int ct = 0; ct < NCM; ++ct)
+                    macc[w][ct][q] = mfma16x16x4(a[ct], s4[q], macc[w][ct][q]);
+#pragma unroll
+                for (int c = 0; c < NV; ++c) vacc[w][q][c] = fmaf(s4[q], hv[c], vacc[w][q][c]);
+            }
+        }
+    };
+
+    // rows [jb, je) of S; EDGE (compile time): the workgroup's column tile
+    // crosses n, so loaded values past column n are zeroed
+    auto run_rows = [&](int jb, int je, auto edge_c) {
+        constexpr bool EDGE = decltype(edge_c)::value;
+        int j0 = jb;
+        for (; j0 + 4 * U <= je; j0 += 4 * U) {
+            float4 sv[U][CW];
+            float a[U][NCM1];
+            float hv[U][NV1];
 #pragma unroll
             for (int u = 0; u < U; ++u) {
-                if (col + 1 >= n) sv[u].y = 0.f;
-                if (col + 2 >= n) sv[u].z = 0.f;
-                if (col + 3 >= n) sv[u].w = 0.f;
+                const int64_t j = j0 + 4 * u + r;
+                load_s(j, EDGE, sv[u]);
+                load_x(j, true, a[u], hv[u]);
             }
-        }
 #pragma unroll
-        for (int u = 0; u < U; ++u) {
-#pragma unroll
-            for (int ct = 0; ct < NC; ++ct) {
-                acc[ct][0] = mfma16x16x4(av[u][ct], sv[u].x, acc[ct][0]);
-                acc[ct][1] = mfma16x16x4(av[u][ct], sv[u].y, acc[ct][1]);
-                acc[ct][2] = mfma16x16x4(av[u][ct], sv[u].z, acc[ct][2]);
-                acc[ct][3] = mfma16x16x4(av[u][ct], sv[u].w, acc[ct][3]);
-            }
+            for (int u = 0; u < U; ++u) compute(sv[u], a[u], hv[u]);
         }
+        // ragged tail: a row past the range end reads its first row (a valid
+        // address) and contributes zero
+        for (; j0 < je; j0 += 4) {
+            const bool ok = j0 + r < je;
+            const int64_t j = ok ? (int64_t)(j0 + r) : (int64_t)jb;
+            float4 sv[CW];
+            float a[NCM1];
+            float hv[NV1];
+            load_s(j, EDGE, sv);
+            if (!ok)
+#pragma unroll
+                for (int w = 0; w < CW; ++w) sv[w] = float4{0.f, 0.f, 0.f, 0.f};
+            load_x(j, ok, a, hv);
+            compute(sv, a, hv);
+        }
+    };
+    auto run = [&](int jb, int je) {
+        if (tile_full) run_rows(jb, je, std::false_type{});
+        else run_rows(jb, je, std::true_type{});
+    };
+    int jb, je;
+    if (SEG) {
+        for (int g = 0; split_segment(rp, split, g, jb, je); ++g) run(jb, je);
+    } else {
+        split_segment(rp, split, 0, jb, je);
+        run(jb, je);
     }
-    // ragged tail: groups with rows past the split end contribute zeros
-    for (; j0 < je; j0 += 4) {
-        const int j = j0 + r;
-        const bool ok = j < je;
-        float4 s4 = float4{0.f, 0.f, 0.f, 0.f};
-        if (ok && colok) s4 = *reinterpret_cast<const float4*>(Sc + (int64_t)j * lds);
-        if (!colfull) {
-            if (col + 1 >= n) s4.y = 0.f;
-            if (col + 2 >= n) s4.z = 0.f;
-            if (col + 3 >= n) s4.w = 0.f;
-        }
-        float av[NC];
-#pragma unroll
-        for (int ct = 0; ct < NC; ++ct) {
-            const int c = 16 * ct + cl;
-            float v = 0.f;
-            if (ok && c < width) {
-                v = X[(int64_t)j * width + c];
-                if (DIFF) v -= Xa[(int64_t)j * width + c];
-            }
-            av[ct] = v;
-        }
-#pragma unroll
-        for (int ct = 0; ct < NC; ++ct) {
-            acc[ct][0] = mfma16x16x4(av[ct], s4.x, acc[ct][0]);
-            acc[ct][1] = mfma16x16x4(av[ct], s4.y, acc[ct][1]);
-            acc[ct][2] = mfma16x16x4(av[ct], s4.z, acc[ct][2]);
-            acc[ct][3] = mfma16x16x4(av[ct], s4.w, acc[ct][3]);
-        }
-    }
-    }  // segments
 
-    // lane holds, for tile (ct, q), output columns c = 16 ct + 4 r + 0..3 of
-    // row i = col + q: one aligned float4 store each.
+    // Output rows i = colbase + 64 w + q. MFMA tile ct: this lane holds
+    // columns 16 ct + 4 r .. +3. Vector-ALU columns: the four row lanes
+    // r = 0..3 hold partial sums over their rows; fold them with two xor
+    // shuffles, then lane r writes columns c_v + NV/4 r .. + NV/4 - 1.
     float* __restrict__ dst = part + (int64_t)split * ((int64_t)n * ldp);
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-        const int i = col + q;
-        if (i < n) {
+    for (int w = 0; w < CW; ++w)
 #pragma unroll
-            for (int ct = 0; ct < NC; ++ct) {
-                const int c0 = 16 * ct + 4 * r;
-                if (c0 < ldp) {
-                    const floatx4 v = acc[ct][q];
-                    *reinterpret_cast<float4*>(dst + (int64_t)i * ldp + c0) =
-                        float4{v[0], v[1], v[2], v[3]};
+        for (int q = 0; q < 4; ++q) {
+#pragma unroll
+            for (int c = 0; c < NV; ++c) {
+                float v = vacc[w][q][c];
+                v += __shfl_xor(v, 16, 64);
+                v += __shfl_xor(v, 32, 64);
+                vacc[w][q][c] = v;
+            }
+            const int i = colbase + 64 * w + q;
+            if (i < n) {
+                float* row = dst + (int64_t)i * ldp;
+#pragma unroll
+                for (int ct = 0; ct < NCM; ++ct) {
+                    const int c0 = 16 * ct + 4 * r;
+                    if (c0 < ldp) {
+                        const floatx4 v = macc[w][ct][q];
+                        *reinterpret_cast<float4*>(row + c0) = float4{v[0], v[1], v[2], v[3]};
+                    }
+                }
+                if (NV > 0) {
+                    constexpr int per = NV / 4;  // 1 or 2 columns per row lane
+#pragma unroll
+                    for (int e = 0; e < per; ++e) {
+                        float v = 0.f;
+#pragma unroll
+                        for (int rr = 0; rr < 4; ++rr)
+                            if (r == rr) v = vacc[w][q][per * rr + e];
+                        const int c = c_v + per * r + e;
+                        if (c < ldp) row[c] = v;
+                    }
                 }
             }
         }
-    }
 }
 
-template <int NC>
-static hipError_t launch_sh_nc(const float* S, int64_t lds, const float* X, const float* Xa,
-                               int width, const RowPlan& rp, int nsplit, float* part, int ldp,
-                               hipStream_t st) {
-    const int ntiles = (rp.n + kShTileCols - 1) / kShTileCols;
+template <int NCM, int NV, int CW, bool DIFF, bool SEG>
+static hipError_t launch_sh_t(const float* S, int64_t lds, const float* X, const float* Xa,
+                              int width, const RowPlan& rp, int nsplit, float* part, int ldp,
+                              hipStream_t st) {
+    const int ntiles = (rp.n + 256 * CW - 1) / (256 * CW);
     dim3 grid((unsigned)ntiles * (unsigned)nsplit);
-    if (Xa)
-        hipLaunchKernelGGL((sh_panel_kernel<NC, true>), grid, dim3(256), 0, st, S, lds, X, Xa,
-                           width, rp, nsplit, part, ldp);
+    bool xvec = NV > 0 && width % 4 == 0 && 16 * NCM + NV <= width &&
+                (reinterpret_cast<uintptr_t>(X) % 16) == 0 &&
+                (!Xa || (reinterpret_cast<uintptr_t>(Xa) % 16) == 0);
+    if (NV > 0 && xvec)
+        hipLaunchKernelGGL((sh_panel_kernel<NCM, NV, CW, DIFF, (NV > 0), SEG>), grid, dim3(256), 0,
+                           st, S, lds, X, Xa, width, rp, nsplit, part, ldp);
     else
-        hipLaunchKernelGGL((sh_panel_kernel<NC, false>), grid, dim3(256), 0, st, S, lds, X,
-                           nullptr, width, rp, nsplit, part, ldp);
+        hipLaunchKernelGGL((sh_panel_kernel<NCM, NV, CW, DIFF, false, SEG>), grid, dim3(256), 0, st,
+                           S, lds, X, Xa, width, rp, nsplit, part, ldp);
     return hipGetLastError();
 }
 
+template <int NCM, int NV, int CW>
+static hipError_t launch_sh_any(const float* S, int64_t lds, const float* X, const float* Xa,
+                                int width, const RowPlan& rp, int nsplit, float* part, int ldp,
+                                hipStream_t st) {
+    if (!Xa) return launch_sh_t<NCM, NV, CW, false, false>(S, lds, X, Xa, width, rp, nsplit, part, ldp, st);
+    // the Block-SVRG correction streams (H - H~): fit widths only (k <= 64)
+    if constexpr (16 * NCM + NV <= kMaxK) {
+        const bool seg = rp.blocks != nullptr && rp.sub == 1 && rp.bps > 1;
+        if (seg) return launch_sh_t<NCM, NV, CW, true, true>(S, lds, X, Xa, width, rp, nsplit, part, ldp, st);
+        return launch_sh_t<NCM, NV, CW, true, false>(S, lds, X, Xa, width, rp, nsplit, part, ldp, st);
+    }
+    return hipErrorInvalidValue;
+}
+
+// Split a width into full 16-column MFMA tiles plus a vector-ALU remainder of
+// 4 or 8 columns (a remainder above 8 takes one more, padded, MFMA tile).
 hipError_t launch_sh_panel(const float* S, int64_t lds, const float* X, const float* Xa,
                            int width, const RowPlan& rp, int nsplit, float* part, int ldp,
                            hipStream_t st) {
-    const int nc = (width + 15) / 16;
-    switch (nc) {
-        case 1: return launch_sh_nc<1>(S, lds, X, Xa, width, rp, nsplit, part, ldp, st);
-        case 2: return launch_sh_nc<2>(S, lds, X, Xa, width, rp, nsplit, part, ldp, st);
-        case 3: return launch_sh_nc<3>(S, lds, X, Xa, width, rp, nsplit, part, ldp, st);
-        case 4: return launch_sh_nc<4>(S, lds, X, Xa, width, rp, nsplit, part, ldp, st);
-        case 5: return launch_sh_nc<5>(S, lds, X, Xa, width, rp, nsplit, part, ldp, st);
-        case 6: return launch_sh_nc<6>(S, lds, X, Xa, width, rp, nsplit, part, ldp, st);
-        case 7: return launch_sh_nc<7>(S, lds, X, Xa, width, rp, nsplit, part, ldp, st);
-        case 8: return launch_sh_nc<8>(S, lds, X, Xa, width, rp, nsplit, part, ldp, st);
-        default: return hipErrorInvalidValue;
-    }
+    int ncm = width / 16;
+    int rem = width - 16 * ncm;
+    int nv = rem == 0 ? 0 : (rem <= 4 ? 4 : (rem <= 8 ? 8 : 0));
+    if (rem > 8) ++ncm;
+#define SH_CASE(M, V, C) \
+    if (ncm == M && nv == V) return launch_sh_any<M, V, C>(S, lds, X, Xa, width, rp, nsplit, part, ldp, st);
+    SH_CASE(0, 4, 2) SH_CASE(0, 8, 2)
+    SH_CASE(1, 0, 2) SH_CASE(1, 4, 2) SH_CASE(1, 8, 2)
+    SH_CASE(2, 0, 2) SH_CASE(2, 4, 2) SH_CASE(2, 8, 2)
+    SH_CASE(3, 0, 1) SH_CASE(3, 4, 1) SH_CASE(3, 8, 1)
+    SH_CASE(4, 0, 1) SH_CASE(4, 4, 1) SH_CASE(4, 8, 1)
+    SH_CASE(5, 0, 1) SH_CASE(5, 4, 1) SH_CASE(5, 8, 1)
+    SH_CASE(6, 0, 1) SH_CASE(6, 4, 1) SH_CASE(6, 8, 1)
+    SH_CASE(7, 0, 1) SH_CASE(7, 4, 1) SH_CASE(7, 8, 1)
+    SH_CASE(8, 0, 1)
+#undef SH_CASE
+    return hipErrorInvalidValue;
 }
 
 // P = sum of the split partials in split order; optional fp64 <Hdot, P> per block.

@@ -14,7 +14,7 @@ constexpr int kShTileCols = 256;  // columns of S per S.H workgroup (4 waves x 6
 constexpr int kUpdRows = 64;      // rows per workgroup of the fused update kernel
 constexpr int kGramTile = 128;    // S-build workgroup tile (2 x 2 waves of 64 x 64)
 
-constexpr int kMaxSplits = 16;   // row splits of one S.H pass (fixed-order sum)
+constexpr int kMaxSplits = 32;   // row splits of one S.H pass (fixed-order sum)
 
 // Which rows of S one split of the S.H pass streams.
 //  contiguous (blocks == nullptr): split s covers

@@ -121,8 +121,8 @@ struct FullPlan {
     int nsplit;
 };
 FullPlan full_plan(int n) {
-    // at most 16 splits, at least 64 rows each: one output accumulates at most
-    // ceil(n/16) rows in fp32 before the fixed-order split sum
+    // at most kMaxSplits splits, at least 64 rows each: one output accumulates
+    // at most ceil(n / kMaxSplits) rows in fp32 before the fixed-order split sum
     int rps = (int)round_up(std::max<int64_t>(64, cdiv(n, kMaxSplits)), 4);
     FullPlan fp;
     fp.nsplit = (int)cdiv(n, rps);

@@ -234,3 +234,25 @@ def test_fit_deterministic(torch, api, c1):
     b = api.fit(Sd, w.k, solver="block_svrg", phi0=0.5, block_rows=256, max_iters=60, seed=3)
     assert torch.equal(a.H, b.H)
     np.testing.assert_array_equal(a.f_trace, b.f_trace)
+
+
+def test_fit_block_svrg_multiblock_splits(torch, api):
+    """48 of 64 row blocks per sampled step: each split of the sampled pass
+    covers two blocks (the multi-block path of the S.H kernel)."""
+    w = synth.student_factor(n=4096, k=12, T=252, seed=5, min_size=64)
+    S = oracle.abs_corr(w.X).astype(np.float32)
+    S64 = S.astype(np.float64)
+    res = api.fit(S_to_dev(S, torch), w.k, solver="block_svrg", phi0=0.75, block_rows=64,
+                  max_iters=60, tol_rel=0.0, seed=4)
+    m = S64.mean()
+    H0 = oracle.init_uniform(w.n, w.k, oracle.init_scale_matched(m, w.k), 4)
+    ref = oracle.fit_adaptgrow(S64, H0, oracle.default_lr(m, w.k), 60,
+                               solver=oracle.SOLVER_BLOCK_SVRG, phi0=0.75, block_rows=64,
+                               tol=0.0, seed=4)
+    assert res.report["n_blocks"] == 64 and res.report["start_branch"] == 1
+    fg, fr = np.asarray(res.f_trace), np.asarray(ref["f"])
+    assert np.array_equal(np.isnan(fg), np.isnan(fr))
+    ex = ~np.isnan(fr)
+    assert traj_rel(fg[ex], fr[ex], float((S64 ** 2).sum())).max() <= 1e-3
+    ok, a = labels_agree(res.H.cpu().numpy(), ref["H"])
+    assert ok, a

@@ -48,8 +48,11 @@ def test_labels_empty(torch, api):
 
 
 # ---- S.H pass -----------------------------------------------------------------
-SH_CASES = [(1, 1), (5, 2), (64, 16), (257, 8), (1000, 24), (1000, 33), (1100, 80),
-            (700, 128), (4099, 24), (8192, 24)]
+# every MFMA-tile / vector-ALU split of the width (4 or 8 vector columns, a
+# padded tile for remainders above 8), ragged n, one and two column groups
+SH_CASES = [(1, 1), (5, 2), (300, 4), (301, 12), (333, 14), (64, 16), (257, 8), (520, 20),
+            (1000, 24), (600, 30), (1000, 33), (777, 40), (2000, 48), (1023, 56), (900, 64),
+            (1100, 80), (900, 100), (900, 112), (700, 128), (4099, 24), (8192, 24)]
 
 
 @pytest.mark.parametrize("n,k", SH_CASES)
