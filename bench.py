@@ -87,6 +87,22 @@ def cpu_baseline(w, k, rows):
             "seconds_per_iter": per_iter}
 
 
+def measured_traffic():
+    """HBM bytes per launch of the full S.H pass from the committed rocprofv3
+    counter summary, if the kernel source is the one those counters were taken
+    on (else None)."""
+    import hashlib
+    path = os.path.join(ROOT, "profiles", "sh_panel_n100000_k24_traffic.json")
+    try:
+        rec = json.load(open(path))
+        src = open(os.path.join(ROOT, rec["source"]), "rb").read()
+    except (OSError, KeyError, ValueError):
+        return None
+    if hashlib.sha256(src).hexdigest() != rec.get("source_sha256"):
+        return None
+    return rec["traffic_bytes_per_launch"]
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -194,7 +210,8 @@ def main():
                    "solver": args.solver, "probe_p": args.probe_p, "tol_rel": 1e-6,
                    "parallelism": "single-gpu"},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": achieved / HBM_PEAK_GBS, "traffic": None,
+                     "frac": achieved / HBM_PEAK_GBS,
+                     "traffic": measured_traffic() if args.workload == "tfactor_n100000_k24" else None,
                      "kernel": "sh_panel_kernel (full S.H pass)", "avg_ms": sh_ms,
                      "bytes_per_launch": sh_bytes},
         "job": {"fit_iterations": rep["iterations"], "converged": bool(rep["converged"]),
