@@ -68,7 +68,7 @@ def cpu_baseline(w, k, rows):
     reps = 3
     t0 = time.perf_counter()
     for _ in range(reps):
-        P_rows, _ = oracle.sh_product(S_rows, H)
+        P_rows, _ = oracle.sh_product(S_rows, H, rows=np.arange(rows))
     t_sh = (time.perf_counter() - t0) / reps
     P = np.zeros((n, k))
     P[:rows] = P_rows

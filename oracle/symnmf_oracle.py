@@ -178,11 +178,16 @@ def default_lr(S_mean, k):
 # --------------------------------------------------------------------------
 
 
-def sh_product(S, H):
+def sh_product(S, H, rows=None):
     """P = S H and tr(H^T S H) = sum_i <H_i, P_i> (the product every full-batch
-    step needs; P1 "Factorization at scale")."""
-    P = np.asarray(S, dtype=np.float64) @ np.asarray(H, dtype=np.float64)
-    return P, float((np.asarray(H, dtype=np.float64) * P).sum())
+    step needs; P1 "Factorization at scale").
+
+    With ``rows`` given, ``S`` holds only those rows of the n x n matrix and
+    the result is those rows of S H and their terms of the trace."""
+    H = np.asarray(H, dtype=np.float64)
+    P = np.asarray(S, dtype=np.float64) @ H
+    Hr = H if rows is None else H[np.asarray(rows)]
+    return P, float((Hr * P).sum())
 
 
 def objective_explicit(S, H):

@@ -125,3 +125,14 @@ def test_default_init_and_lr_readings():
     a = oracle.init_scale_matched(0.06, 24)
     assert 24 * (a / 2) ** 2 == pytest.approx(0.06)
     assert oracle.default_lr(0.06, 24) == pytest.approx(a / 2)
+
+
+def test_sh_product_rows_match_full():
+    S = _rand_sym(30, 13)
+    H = np.random.default_rng(14).random((30, 4))
+    P, tr = oracle.sh_product(S, H)
+    rows = np.array([3, 7, 29])
+    Pr, trr = oracle.sh_product(S[rows], H, rows=rows)
+    np.testing.assert_allclose(Pr, P[rows], rtol=1e-14)
+    assert trr == pytest.approx(float((H[rows] * P[rows]).sum()), rel=1e-13)
+    assert tr == pytest.approx(float(np.trace(H.T @ S @ H)), rel=1e-13)
