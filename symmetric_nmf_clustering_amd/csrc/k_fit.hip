@@ -13,7 +13,7 @@
 
 namespace symnmf {
 
-// ---- S statistics: per 64-row block, sum S and sum S^2 (fp64) ---------------
+// ---- S statistics: per 64-row block, sum S and sum S^2 (accumulated in fp64) ---
 __global__ __launch_bounds__(256) void s_stats_kernel(const float* __restrict__ S, int64_t lds,
                                                       int n, double* __restrict__ part2) {
     __shared__ double red[4];
@@ -22,14 +22,11 @@ __global__ __launch_bounds__(256) void s_stats_kernel(const float* __restrict__ 
     double s1 = 0.0, s2 = 0.0;
     for (int rr = 0; rr < rows; ++rr) {
         const float* row = S + (int64_t)(row0 + rr) * lds;
-        float a1 = 0.f, a2 = 0.f;  // <= n/256 terms per thread per row
         for (int c = threadIdx.x; c < n; c += 256) {
-            const float v = row[c];
-            a1 += v;
-            a2 += v * v;
+            const double v = (double)row[c];
+            s1 += v;
+            s2 += v * v;
         }
-        s1 += a1;
-        s2 += a2;
     }
     const double t1 = block_sum256(s1, red);
     const double t2 = block_sum256(s2, red);

@@ -1,0 +1,94 @@
+"""Full-size parity at n = 100 000, k = 24 (40 GB S), in the launch configuration
+the benchmark times. The oracle computes sampled rows one by one from the
+returns window; whole-matrix facts are checked as properties that hold at any
+size."""
+import numpy as np
+import pytest
+
+import oracle
+from symmetric_nmf_clustering_amd import synth
+from tests.gpu_util import require_gpu, s_close, to_dev
+
+pytestmark = pytest.mark.gpu
+
+N, K = 100000, 24
+
+
+@pytest.fixture(scope="module")
+def big():
+    torch = require_gpu()
+    from symmetric_nmf_clustering_amd import api
+    free, total = torch.cuda.mem_get_info()
+    if free < 48e9:
+        pytest.skip("needs ~48 GB of free device memory")
+    w = synth.workload("tfactor_n100000_k24")
+    S, fro = api.build_S(to_dev(w.X, torch), "abscorr")
+    rng = np.random.default_rng(11)
+    rows = np.unique(np.concatenate([[0, 1, 511, 512, 4095, 50000, N - 2, N - 1],
+                                     rng.integers(0, N, 40)]))
+    yield torch, api, w, S, fro, rows
+    del S
+    torch.cuda.empty_cache()
+
+
+def test_fullsize_S_rows_and_symmetry(big):
+    torch, api, w, S, fro, rows = big
+    got = S[torch.from_numpy(rows).cuda()].cpu().numpy()
+    ref = oracle.abs_corr_rows(w.X, rows)
+    ok, worst = s_close(got, ref)
+    assert ok, worst
+    # bitwise symmetric: row i equals column i
+    cols = S[:, torch.from_numpy(rows).cuda()].cpu().numpy().T
+    assert np.array_equal(got, cols)
+    assert np.isfinite(fro) and fro > 0
+
+
+def test_fullsize_sh_rows(big):
+    torch, api, w, S, fro, rows = big
+    H = synth.random_factor(N, K, seed=3, scale=0.1)
+    P, tr = api.sh(S, to_dev(H, torch))
+    Pg = P.cpu().numpy().astype(np.float64)
+    S_rows = oracle.abs_corr_rows(w.X, rows)
+    Pr, _ = oracle.sh_product(S_rows, H, rows=rows)
+    rel = np.abs(Pg[rows] - Pr) / np.abs(Pr)
+    assert rel.max() <= 1e-4, rel.max()
+    # tr(H^T S H) = sum_i <H_i, P_i> over all rows (a property of the outputs)
+    assert abs(tr - float((H.astype(np.float64) * Pg).sum())) <= 1e-9 * abs(tr)
+
+
+def test_fullsize_first_step_and_objective(big):
+    torch, api, w, S, fro, rows = big
+    lr = 0.05
+    res = api.fit(S, K, solver="full", init="uniform", init_scale=0.1, seed=5, lr=lr,
+                  max_iters=1, tol_rel=0.0)
+    H0 = oracle.init_uniform(N, K, 0.1, 5)
+    K0 = H0.T @ H0
+    S_rows = oracle.abs_corr_rows(w.X, rows)
+    P_rows, _ = oracle.sh_product(S_rows, H0, rows=rows)
+    g = 4.0 * (H0[rows] @ K0 - P_rows)
+    H1_ref = np.maximum(H0[rows] - lr * g / (np.abs(g) + 1e-8), 0.0)
+    H1 = res.H.cpu().numpy()[rows].astype(np.float64)
+    # the first AdaGrad step is lr * sign(g) unless |g| is tiny; compare where
+    # the sign is decided well above the fp32 noise of g
+    decided = np.abs(g) > 1e-3 * np.abs(g).max()
+    assert decided.mean() > 0.9
+    assert np.abs(H1 - H1_ref)[decided].max() <= 1e-5
+    # f_0 by the trace identity equals ||S||^2 - 2 tr + ||K0||^2 with the
+    # build's ||S||^2 and the S.H pass's trace
+    _, tr0 = api.sh(S, to_dev(H0, torch))
+    f0 = fro - 2.0 * tr0 + float((K0 * K0).sum())
+    assert abs(res.f_trace[0] - f0) <= 1e-6 * f0
+    assert abs(res.report["S_fro2"] - fro) <= 1e-9 * fro
+
+
+def test_fullsize_labels_property(big):
+    torch, api, w, S, fro, rows = big
+    res = api.fit(S, K, solver="full", max_iters=30, tol_rel=0.0, seed=0)
+    lab = api.labels(res.H).cpu().numpy()
+    H = res.H.cpu().numpy()
+    # argmax property on every row, lowest index on ties
+    mx = H.max(axis=1)
+    assert np.all(H[np.arange(N), lab] == mx)
+    first = np.argmax(H == mx[:, None], axis=1)
+    assert np.array_equal(first, lab)
+    assert res.H.min().item() >= 0.0
