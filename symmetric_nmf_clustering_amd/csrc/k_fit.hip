@@ -319,76 +319,87 @@ hipError_t launch_count_zero_rows(const float* H, int n, int k, int* out, hipStr
 }
 
 // ---- probe helpers ---------------------------------------------------------------
-// C = A^T B partials over blocks of kCgRows rows; fp64 accumulation.
-constexpr int kCgRows = 512;
-constexpr int kCgChunk = 32;
+// C = A^T B partials over blocks of kCgRows rows. Thread (tx, ty) of a 16 x 16
+// grid owns the TB x TB block of C at rows tx TB.., columns ty TB.. (w <= 16 TB):
+// per staged row it reads TB values of A and TB of B from LDS and does TB^2
+// FMAs. Each block's fp32 partial covers kCgRows rows; the blocks are folded in
+// fp64 in a fixed order.
+constexpr int kCgRows = 64;
 
+template <int TB>
 __global__ __launch_bounds__(256) void crossgram_kernel(const float* __restrict__ A,
                                                         const float* __restrict__ B, int n, int w,
-                                                        double* __restrict__ part) {
-    extern __shared__ float cg[];
-    float* As = cg;                 // kCgChunk x w
-    float* Bs = cg + kCgChunk * w;  // kCgChunk x w
+                                                        float* __restrict__ part) {
+    __shared__ float As[kCgRows][16 * TB + 1];
+    __shared__ float Bs[kCgRows][16 * TB + 1];
     const int row0 = blockIdx.x * kCgRows;
-    const int rend = min(n, row0 + kCgRows);
+    const int rows = min(kCgRows, n - row0);
     const int tid = threadIdx.x;
-    // each thread owns entries idx = tid + 256 m of the w x w result
-    constexpr int kMaxOwn = (kMaxWidth * kMaxWidth + 255) / 256;
-    double acc[kMaxOwn];
-    const int own = (w * w + 255) / 256;
-#pragma unroll
-    for (int m = 0; m < kMaxOwn; ++m) acc[m] = 0.0;
-    for (int r0 = row0; r0 < rend; r0 += kCgChunk) {
-        const int rows = min(kCgChunk, rend - r0);
-        __syncthreads();
-        for (int e = tid; e < kCgChunk * w; e += 256) {
-            const int i = e / w;
-            As[e] = (i < rows) ? A[(int64_t)(r0 + i) * w + (e % w)] : 0.f;
-            Bs[e] = (i < rows) ? B[(int64_t)(r0 + i) * w + (e % w)] : 0.f;
-        }
-        __syncthreads();
-#pragma unroll
-        for (int m = 0; m < kMaxOwn; ++m) {
-            if (m < own) {
-                const int idx = tid + 256 * m;
-                if (idx < w * w) {
-                    const int x = idx / w;
-                    const int y = idx % w;
-                    float s = 0.f;  // <= 32 terms in fp32, then fp64
-                    for (int i = 0; i < kCgChunk; ++i) s = fmaf(As[i * w + x], Bs[i * w + y], s);
-                    acc[m] += (double)s;
-                }
-            }
-        }
+    for (int e = tid; e < kCgRows * w; e += 256) {
+        const int i = e / w, c = e % w;
+        As[i][c] = i < rows ? A[(int64_t)(row0 + i) * w + c] : 0.f;
+        Bs[i][c] = i < rows ? B[(int64_t)(row0 + i) * w + c] : 0.f;
     }
-    double* out = part + (int64_t)blockIdx.x * w * w;
+    __syncthreads();
+    const int tx = tid & 15, ty = tid >> 4;
+    float acc[TB][TB];
 #pragma unroll
-    for (int m = 0; m < kMaxOwn; ++m) {
-        const int idx = tid + 256 * m;
-        if (m < own && idx < w * w) out[idx] = acc[m];
+    for (int a = 0; a < TB; ++a)
+#pragma unroll
+        for (int b = 0; b < TB; ++b) acc[a][b] = 0.f;
+    const int x0 = tx * TB, y0 = ty * TB;
+    if (x0 < w && y0 < w) {
+        for (int i = 0; i < kCgRows; ++i) {
+            float av[TB], bv[TB];
+#pragma unroll
+            for (int a = 0; a < TB; ++a) av[a] = (x0 + a < w) ? As[i][x0 + a] : 0.f;
+#pragma unroll
+            for (int b = 0; b < TB; ++b) bv[b] = (y0 + b < w) ? Bs[i][y0 + b] : 0.f;
+#pragma unroll
+            for (int a = 0; a < TB; ++a)
+#pragma unroll
+                for (int b = 0; b < TB; ++b) acc[a][b] = fmaf(av[a], bv[b], acc[a][b]);
+        }
+        float* out = part + (int64_t)blockIdx.x * w * w;
+#pragma unroll
+        for (int a = 0; a < TB; ++a)
+#pragma unroll
+            for (int b = 0; b < TB; ++b)
+                if (x0 + a < w && y0 + b < w) out[(x0 + a) * w + y0 + b] = acc[a][b];
     }
 }
 
-__global__ void crossgram_final_kernel(const double* __restrict__ part, int nblk, int ww,
-                                       double* __restrict__ C) {
-    const int idx = blockIdx.x * blockDim.x + threadIdx.x;
-    if (idx >= ww) return;
+// C[idx] = sum over blocks of part[b][idx] in fp64, fixed order: thread t of
+// workgroup idx sums blocks t, t + 256, ...; then a fixed-order tree.
+__global__ __launch_bounds__(256) void crossgram_final_kernel(const float* __restrict__ part,
+                                                              int nblk, int ww,
+                                                              double* __restrict__ C) {
+    __shared__ double red[4];
+    const int idx = blockIdx.x;
     double s = 0.0;
-    for (int b = 0; b < nblk; ++b) s += part[(int64_t)b * ww + idx];
-    C[idx] = s;
+    for (int b = threadIdx.x; b < nblk; b += 256) s += (double)part[(int64_t)b * ww + idx];
+    s = block_sum256(s, red);
+    if (threadIdx.x == 0) C[idx] = s;
 }
 
 int crossgram_blocks(int n) { return (n + kCgRows - 1) / kCgRows; }
 
-hipError_t launch_crossgram(const float* A, const float* B, int n, int w, double* part,
-                            int nblk, double* C, hipStream_t st) {
-    const size_t sm = (size_t)2 * kCgChunk * w * sizeof(float);
-    hipLaunchKernelGGL(crossgram_kernel, dim3(nblk), dim3(256), sm, st, A, B, n, w, part);
+hipError_t launch_crossgram(const float* A, const float* B, int n, int w, float* part, int nblk,
+                            double* C, hipStream_t st) {
+    const int tb = (w + 15) / 16;
+    switch (tb) {
+#define CG_CASE(T)                                                                            \
+    case T:                                                                                   \
+        hipLaunchKernelGGL(crossgram_kernel<T>, dim3(nblk), dim3(256), 0, st, A, B, n, w, part); \
+        break;
+        CG_CASE(1) CG_CASE(2) CG_CASE(3) CG_CASE(4) CG_CASE(5) CG_CASE(6) CG_CASE(7) CG_CASE(8)
+#undef CG_CASE
+        default: return hipErrorInvalidValue;
+    }
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     const int ww = w * w;
-    hipLaunchKernelGGL(crossgram_final_kernel, dim3((ww + 255) / 256), dim3(256), 0, st, part,
-                       nblk, ww, C);
+    hipLaunchKernelGGL(crossgram_final_kernel, dim3(ww), dim3(256), 0, st, part, nblk, ww, C);
     return hipGetLastError();
 }
 

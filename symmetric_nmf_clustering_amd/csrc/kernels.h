@@ -99,9 +99,9 @@ hipError_t launch_count_zero_rows(const float* H, int n, int k, int* out, hipStr
 hipError_t launch_labels(const float* H, int64_t n, int k, int32_t* labels, hipStream_t st);
 
 // ---- probe helpers ----------------------------------------------------------
-// C = A^T B (w x w, fp64) for n x w matrices A, B (ld w): per-block partials then
-// a fixed-order reduction into C.
-hipError_t launch_crossgram(const float* A, const float* B, int n, int w, double* part,
+// C = A^T B (w x w, fp64) for n x w matrices A, B (ld w): per-block fp32
+// partials, then a fixed-order fp64 reduction into C.
+hipError_t launch_crossgram(const float* A, const float* B, int n, int w, float* part,
                             int nblk, double* C, hipStream_t st);
 int crossgram_blocks(int n);
 // Q[i][:] = Y[i][:] M (M w x w fp32, row-major)

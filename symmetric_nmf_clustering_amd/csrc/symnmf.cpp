@@ -248,8 +248,8 @@ size_t sh_layout(void* ws, int64_t n, int width, ShLayout* L) {
 }
 
 struct ProbeLayout {
-    float *Q, *Y, *part, *M;
-    double *cg_part, *C;
+    float *Q, *Y, *part, *M, *cg_part;
+    double* C;
 };
 int probe_width(int p) { return (int)round_up(p + 16, 16); }
 size_t probe_layout(void* ws, int64_t n, int p, ProbeLayout* L) {
@@ -261,7 +261,7 @@ size_t probe_layout(void* ws, int64_t n, int p, ProbeLayout* L) {
     l.Y = c.take<float>((size_t)n * w);
     l.part = c.take<float>((size_t)fp.nsplit * n * ldp_of(w));
     l.M = c.take<float>((size_t)w * w);
-    l.cg_part = c.take<double>((size_t)crossgram_blocks((int)n) * w * w);
+    l.cg_part = c.take<float>((size_t)crossgram_blocks((int)n) * w * w);
     l.C = c.take<double>((size_t)w * w);
     if (L) *L = l;
     return c.off;
