@@ -8,6 +8,8 @@
 // scale" (objective by the trace identity, no n x n intermediates).
 #include <math.h>
 
+#include <algorithm>
+
 #include "common.h"
 #include "kernels.h"
 
@@ -302,6 +304,30 @@ hipError_t launch_labels(const float* H, int64_t n, int k, int32_t* labels, hipS
     if (n <= 0) return hipSuccess;
     hipLaunchKernelGGL(labels_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, H, n,
                        k, labels);
+    return hipGetLastError();
+}
+
+// Rows of the selected blocks only: blockIdx.y is the block's position in the
+// list, blockIdx.x strides over its block_rows * k entries.
+__global__ __launch_bounds__(256) void block_diff_kernel(const float* __restrict__ H,
+                                                         const float* __restrict__ Ha,
+                                                         const int* __restrict__ blocks,
+                                                         int block_rows, int n, int k,
+                                                         float* __restrict__ D) {
+    const int64_t base = (int64_t)blocks[blockIdx.y] * block_rows;
+    const int64_t end = min((int64_t)n, base + block_rows) * k;
+    for (int64_t e = base * k + (int64_t)blockIdx.x * 256 + threadIdx.x; e < end;
+         e += (int64_t)gridDim.x * 256)
+        D[e] = H[e] - Ha[e];
+}
+
+hipError_t launch_block_diff(const float* H, const float* Ha, const int* blocks, int nsel,
+                             int block_rows, int n, int k, float* D, hipStream_t st) {
+    if (nsel <= 0) return hipSuccess;
+    const int64_t per = (int64_t)block_rows * k;
+    const unsigned gx = (unsigned)std::min<int64_t>(64, (per + 255) / 256);
+    hipLaunchKernelGGL(block_diff_kernel, dim3(gx, (unsigned)nsel), dim3(256), 0, st, H, Ha,
+                       blocks, block_rows, n, k, D);
     return hipGetLastError();
 }
 

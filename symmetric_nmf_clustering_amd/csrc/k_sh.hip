@@ -61,13 +61,23 @@ __device__ __forceinline__ bool split_segment(const RowPlan& rp, int s, int g, i
 // NV columns inside the width). SEG: a split may cover several row blocks
 // (kept out of the common single-range case, where the extra loop level
 // roughly doubles the register footprint).
-template <int NCM, int NV, int CW, bool DIFF, bool XVEC, bool SEG>
+// 4-row groups per main-loop trip. The narrow shapes (CW = 2 with at most one
+// MFMA tile beside the vector-ALU columns, i.e. k <= 24, or MFMA tiles only)
+// are bound by HBM: the more rows of S one wave has in flight the better, and
+// six groups (24 rows, 12 KiB per wave) still leave two waves per SIMD. The
+// wide shapes are bound by the matrix core, and the multi-segment variant
+// carries an extra loop level; both keep two groups (deeper trips only cost
+// occupancy there).
+constexpr int sh_rows_per_trip(int ncm, int nv, int cw, bool seg) {
+    return (cw == 2 && !seg && (ncm <= 1 || nv == 0)) ? 6 : 2;
+}
+
+template <int NCM, int NV, int CW, bool XVEC, bool SEG>
 __global__ __launch_bounds__(256) void sh_panel_kernel(const float* __restrict__ S, int64_t lds,
-                                                       const float* __restrict__ X,
-                                                       const float* __restrict__ Xa, int width,
+                                                       const float* __restrict__ X, int width,
                                                        RowPlan rp, int nsplit,
                                                        float* __restrict__ part, int ldp) {
-    constexpr int U = 2;              // 4-row groups per main-loop trip
+    constexpr int U = sh_rows_per_trip(NCM, NV, CW, SEG);
     constexpr int WCOLS = 64 * CW;    // columns per wave
     constexpr int NCM1 = NCM > 0 ? NCM : 1;
     constexpr int NV1 = NV > 0 ? NV : 1;
@@ -108,28 +118,19 @@ __global__ __launch_bounds__(256) void sh_panel_kernel(const float* __restrict__
     // this lane's X values of row j: MFMA A operands and vector-ALU columns
     auto load_x = [&](int64_t j, bool rowok, float (&a)[NCM1], float (&hv)[NV1]) {
         const float* px = X + j * width;
-        const float* pxa = DIFF ? Xa + j * width : nullptr;
 #pragma unroll
         for (int ct = 0; ct < NCM; ++ct) {
             const int c = 16 * ct + cl;
             const bool ok = rowok && c < width;
             const int off = c < width ? c : 0;
-            float v = px[off];
-            if (DIFF) v -= pxa[off];
+            const float v = px[off];
             a[ct] = ok ? v : 0.f;
         }
         if (NV > 0) {
             if (XVEC) {
 #pragma unroll
                 for (int c4 = 0; c4 < NV; c4 += 4) {
-                    float4 v = *reinterpret_cast<const float4*>(px + c_v + c4);
-                    if (DIFF) {
-                        const float4 va = *reinterpret_cast<const float4*>(pxa + c_v + c4);
-                        v.x -= va.x;
-                        v.y -= va.y;
-                        v.z -= va.z;
-                        v.w -= va.w;
-                    }
+                    const float4 v = *reinterpret_cast<const float4*>(px + c_v + c4);
                     hv[c4 + 0] = rowok ? v.x : 0.f;
                     hv[c4 + 1] = rowok ? v.y : 0.f;
                     hv[c4 + 2] = rowok ? v.z : 0.f;
@@ -140,8 +141,7 @@ __global__ __launch_bounds__(256) void sh_panel_kernel(const float* __restrict__
                 for (int c = 0; c < NV; ++c) {
                     const bool ok = rowok && c_v + c < width;
                     const int off = c_v + c < width ? c_v + c : 0;
-                    float v = px[off];
-                    if (DIFF) v -= pxa[off];
+                    const float v = px[off];
                     hv[c] = ok ? v : 0.f;
                 }
             }
@@ -151,7 +151,10 @@ __global__ __launch_bounds__(256) void sh_panel_kernel(const float* __restrict__
         const float* ps = S + j * lds;
 #pragma unroll
         for (int w = 0; w < CW; ++w) {
-            float4 v = *reinterpret_cast<const float4*>(ps + scol[w]);
+            // S is streamed once per pass: a non-temporal load keeps it from
+            // displacing X, which every column tile of a split re-reads
+            const floatx4 t = __builtin_nontemporal_load(reinterpret_cast<const floatx4*>(ps + scol[w]));
+            float4 v = float4{t[0], t[1], t[2], t[3]};
             if (edge) {
                 const int c0 = colbase + 64 * w;
                 v.x = c0 < n ? v.x : 0.f;
@@ -266,49 +269,44 @@ __global__ __launch_bounds__(256) void sh_panel_kernel(const float* __restrict__
         }
 }
 
-template <int NCM, int NV, int CW, bool DIFF, bool SEG>
-static hipError_t launch_sh_t(const float* S, int64_t lds, const float* X, const float* Xa,
-                              int width, const RowPlan& rp, int nsplit, float* part, int ldp,
-                              hipStream_t st) {
+template <int NCM, int NV, int CW, bool SEG>
+static hipError_t launch_sh_t(const float* S, int64_t lds, const float* X, int width,
+                              const RowPlan& rp, int nsplit, float* part, int ldp, hipStream_t st) {
     const int ntiles = (rp.n + 256 * CW - 1) / (256 * CW);
     dim3 grid((unsigned)ntiles * (unsigned)nsplit);
-    bool xvec = NV > 0 && width % 4 == 0 && 16 * NCM + NV <= width &&
-                (reinterpret_cast<uintptr_t>(X) % 16) == 0 &&
-                (!Xa || (reinterpret_cast<uintptr_t>(Xa) % 16) == 0);
+    const bool xvec = NV > 0 && width % 4 == 0 && 16 * NCM + NV <= width &&
+                      (reinterpret_cast<uintptr_t>(X) % 16) == 0;
     if (NV > 0 && xvec)
-        hipLaunchKernelGGL((sh_panel_kernel<NCM, NV, CW, DIFF, (NV > 0), SEG>), grid, dim3(256), 0,
-                           st, S, lds, X, Xa, width, rp, nsplit, part, ldp);
+        hipLaunchKernelGGL((sh_panel_kernel<NCM, NV, CW, (NV > 0), SEG>), grid, dim3(256), 0, st, S,
+                           lds, X, width, rp, nsplit, part, ldp);
     else
-        hipLaunchKernelGGL((sh_panel_kernel<NCM, NV, CW, DIFF, false, SEG>), grid, dim3(256), 0, st,
-                           S, lds, X, Xa, width, rp, nsplit, part, ldp);
+        hipLaunchKernelGGL((sh_panel_kernel<NCM, NV, CW, false, SEG>), grid, dim3(256), 0, st, S,
+                           lds, X, width, rp, nsplit, part, ldp);
     return hipGetLastError();
 }
 
 template <int NCM, int NV, int CW>
-static hipError_t launch_sh_any(const float* S, int64_t lds, const float* X, const float* Xa,
-                                int width, const RowPlan& rp, int nsplit, float* part, int ldp,
+static hipError_t launch_sh_any(const float* S, int64_t lds, const float* X, int width,
+                                const RowPlan& rp, int nsplit, float* part, int ldp,
                                 hipStream_t st) {
-    if (!Xa) return launch_sh_t<NCM, NV, CW, false, false>(S, lds, X, Xa, width, rp, nsplit, part, ldp, st);
-    // the Block-SVRG correction streams (H - H~): fit widths only (k <= 64)
-    if constexpr (16 * NCM + NV <= kMaxK) {
-        const bool seg = rp.blocks != nullptr && rp.sub == 1 && rp.bps > 1;
-        if (seg) return launch_sh_t<NCM, NV, CW, true, true>(S, lds, X, Xa, width, rp, nsplit, part, ldp, st);
-        return launch_sh_t<NCM, NV, CW, true, false>(S, lds, X, Xa, width, rp, nsplit, part, ldp, st);
-    }
+    // several row blocks per split: sampled passes of fit widths only (k <= 64)
+    const bool seg = rp.blocks != nullptr && rp.sub == 1 && rp.bps > 1;
+    if (!seg) return launch_sh_t<NCM, NV, CW, false>(S, lds, X, width, rp, nsplit, part, ldp, st);
+    if constexpr (16 * NCM + NV <= kMaxK)
+        return launch_sh_t<NCM, NV, CW, true>(S, lds, X, width, rp, nsplit, part, ldp, st);
     return hipErrorInvalidValue;
 }
 
 // Split a width into full 16-column MFMA tiles plus a vector-ALU remainder of
 // 4 or 8 columns (a remainder above 8 takes one more, padded, MFMA tile).
-hipError_t launch_sh_panel(const float* S, int64_t lds, const float* X, const float* Xa,
-                           int width, const RowPlan& rp, int nsplit, float* part, int ldp,
-                           hipStream_t st) {
+hipError_t launch_sh_panel(const float* S, int64_t lds, const float* X, int width,
+                           const RowPlan& rp, int nsplit, float* part, int ldp, hipStream_t st) {
     int ncm = width / 16;
     int rem = width - 16 * ncm;
     int nv = rem == 0 ? 0 : (rem <= 4 ? 4 : (rem <= 8 ? 8 : 0));
     if (rem > 8) ++ncm;
 #define SH_CASE(M, V, C) \
-    if (ncm == M && nv == V) return launch_sh_any<M, V, C>(S, lds, X, Xa, width, rp, nsplit, part, ldp, st);
+    if (ncm == M && nv == V) return launch_sh_any<M, V, C>(S, lds, X, width, rp, nsplit, part, ldp, st);
     SH_CASE(0, 4, 2) SH_CASE(0, 8, 2)
     SH_CASE(1, 0, 2) SH_CASE(1, 4, 2) SH_CASE(1, 8, 2)
     SH_CASE(2, 0, 2) SH_CASE(2, 4, 2) SH_CASE(2, 8, 2)

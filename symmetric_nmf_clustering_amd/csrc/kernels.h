@@ -53,11 +53,16 @@ struct FitDev {
 
 // ---- S.H pass ---------------------------------------------------------------
 // part[s][i][c] (ld ldp = round_up(width, 4), split stride n*ldp) =
-//   sum over rows j of split s of S[j][i] * (X[j][c] - Xa[j][c])   (Xa nullable)
-// which is (S X)[i][c] restricted to those rows, for symmetric S.
-hipError_t launch_sh_panel(const float* S, int64_t lds, const float* X, const float* Xa,
-                           int width, const RowPlan& rp, int nsplit, float* part, int ldp,
-                           hipStream_t st);
+//   sum over rows j of split s of S[j][i] * X[j][c]
+// which is (S X)[i][c] restricted to those rows, for symmetric S. Only the
+// rows of the plan are read from X.
+hipError_t launch_sh_panel(const float* S, int64_t lds, const float* X, int width,
+                           const RowPlan& rp, int nsplit, float* part, int ldp, hipStream_t st);
+// D[j][c] = H[j][c] - Ha[j][c] (fp32) for the rows j of the nsel listed row
+// blocks of block_rows rows (the Block-SVRG correction's input); other rows
+// of D are left as they are.
+hipError_t launch_block_diff(const float* H, const float* Ha, const int* blocks, int nsel,
+                             int block_rows, int n, int k, float* D, hipStream_t st);
 // P[i][c] = sum_s part[s][i][c] (c < width, ld width); if Hdot: tr_part[b] =
 // sum over the rows of block b of <Hdot_i, P_i> (fp64). Blocks of kUpdRows rows.
 hipError_t launch_reduce_partials(const float* part, int nsplit, int n, int width, int ldp,

@@ -270,7 +270,7 @@ size_t probe_layout(void* ws, int64_t n, int p, ProbeLayout* L) {
 struct FitLayout {
     FitDev* fd;
     double* f_trace;
-    float *Hb[2], *Gb[2], *Ha, *Pa, *part, *gram_part;
+    float *Hb[2], *Gb[2], *Ha, *Pa, *D, *part, *gram_part;
     double *tr_part, *stats_part, *stats_out;
     int *blocks, *zero_rows;
 };
@@ -285,6 +285,7 @@ size_t fit_layout(void* ws, int64_t n, int k, int max_iters, int block_rows, Fit
     for (int i = 0; i < 2; ++i) l.Gb[i] = c.take<float>((size_t)n * k);
     l.Ha = c.take<float>((size_t)n * k);
     l.Pa = c.take<float>((size_t)n * k);
+    l.D = c.take<float>((size_t)n * k);
     l.part = c.take<float>((size_t)kMaxSplits * n * ldp_of(k));
     l.gram_part = c.take<float>((size_t)nblk * k * k);
     l.tr_part = c.take<double>((size_t)nblk);
@@ -440,7 +441,7 @@ int symnmf_sh(const float* S, int64_t n, int64_t lds, const float* H, int32_t k,
     const int ldp = ldp_of(k);
     {
         ProfScope ps(SYMNMF_PROF_SH_FULL, 4.0 * n * (double)n + 8.0 * n * k, st);
-        HIPCHK(launch_sh_panel(S, lds, H, nullptr, k, fp.rp, fp.nsplit, L.part, ldp, st));
+        HIPCHK(launch_sh_panel(S, lds, H, k, fp.rp, fp.nsplit, L.part, ldp, st));
     }
     HIPCHK(launch_reduce_partials(L.part, fp.nsplit, (int)n, k, ldp, P, H, L.tr_part, st));
     if (tr_host) {
@@ -587,7 +588,7 @@ int symnmf_spectral_probe(const float* S, int64_t n, int64_t lds, int32_t p, int
     for (it = 1; it <= max_iters; ++it) {
         {
             ProfScope ps(SYMNMF_PROF_SH_PROBE, 4.0 * n * (double)n + 8.0 * n * w, st);
-            HIPCHK(launch_sh_panel(S, lds, Q, nullptr, w, fp.rp, fp.nsplit, L.part, ldp, st));
+            HIPCHK(launch_sh_panel(S, lds, Q, w, fp.rp, fp.nsplit, L.part, ldp, st));
         }
         HIPCHK(launch_reduce_partials(L.part, fp.nsplit, nn, w, ldp, Y, nullptr, nullptr, st));
         HIPCHK(launch_crossgram(Q, Y, nn, w, L.cg_part, nblk, L.C, st));
@@ -758,7 +759,7 @@ int symnmf_fit(const float* S, int64_t n, int64_t lds, int32_t k, const symnmf_f
     auto exact_step = [&](bool write_anchor, int flags) -> int {
         {
             ProfScope ps(SYMNMF_PROF_SH_FULL, sh_bytes, st);
-            HIPCHK(launch_sh_panel(S, lds, L.Hb[cur], nullptr, k, fpl.rp, fpl.nsplit, L.part, ldp, st));
+            HIPCHK(launch_sh_panel(S, lds, L.Hb[cur], k, fpl.rp, fpl.nsplit, L.part, ldp, st));
         }
         UpdateArgs a{};
         a.n = nn; a.k = k; a.ldp = ldp; a.part = L.part; a.nsplit = fpl.nsplit;
@@ -781,7 +782,9 @@ int symnmf_fit(const float* S, int64_t n, int64_t lds, int32_t k, const symnmf_f
         {
             const double rows = std::min<double>((double)nsel * P.block_rows, (double)n);
             ProfScope ps(SYMNMF_PROF_SH_SAMPLED, 4.0 * rows * (double)n + 8.0 * (double)nk, st);
-            HIPCHK(launch_sh_panel(S, lds, L.Hb[cur], L.Ha, k, sp.rp, sp.nsplit, L.part, ldp, st));
+            // D = H - H~ on the sampled rows, then the correction sum over them
+            HIPCHK(launch_block_diff(L.Hb[cur], L.Ha, blocks_dev, nsel, P.block_rows, nn, k, L.D, st));
+            HIPCHK(launch_sh_panel(S, lds, L.D, k, sp.rp, sp.nsplit, L.part, ldp, st));
         }
         UpdateArgs a{};
         a.n = nn; a.k = k; a.ldp = ldp; a.part = L.part; a.nsplit = sp.nsplit;
