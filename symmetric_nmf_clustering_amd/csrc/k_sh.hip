@@ -31,13 +31,19 @@
 
 namespace symnmf {
 
+// How a split's rows are found: contiguous ranges of rows_per_split rows (a
+// full pass), or row blocks of a sampled list with one range per split
+// (blocks cut into `sub` sub-ranges) or several whole blocks per split.
+enum RowMode : int { kRowsContiguous = 0, kRowsBlocks = 1, kRowsBlocksMulti = 2 };
+
 // Row segment `g` of split `s` (at most rp.bps segments); false when none.
+template <int RM>
 __device__ __forceinline__ bool split_segment(const RowPlan& rp, int s, int g, int& jb, int& je) {
-    if (rp.blocks == nullptr) {
+    if constexpr (RM == kRowsContiguous) {
         if (g > 0) return false;
         jb = s * rp.rows_per_split;
         je = min(rp.n, jb + rp.rows_per_split);
-    } else if (rp.sub > 1) {
+    } else if constexpr (RM == kRowsBlocks) {
         if (g > 0) return false;
         const int blk = rp.blocks[s / rp.sub];
         const int base = blk * rp.block_rows;
@@ -55,12 +61,6 @@ __device__ __forceinline__ bool split_segment(const RowPlan& rp, int s, int g, i
     return true;
 }
 
-// NCM MFMA column tiles (16 columns each) plus NV <= 8 columns on the vector
-// ALU, CW float4 column groups per lane (64 CW columns per wave). XVEC: the
-// vector-ALU columns are read as float4s (row pitch a multiple of 4 and all
-// NV columns inside the width). SEG: a split may cover several row blocks
-// (kept out of the common single-range case, where the extra loop level
-// roughly doubles the register footprint).
 // 4-row groups per main-loop trip. The narrow shapes (CW = 2 with at most one
 // MFMA tile beside the vector-ALU columns, i.e. k <= 24, or MFMA tiles only)
 // are bound by HBM: the more rows of S one wave has in flight the better, and
@@ -68,16 +68,20 @@ __device__ __forceinline__ bool split_segment(const RowPlan& rp, int s, int g, i
 // wide shapes are bound by the matrix core, and the multi-segment variant
 // carries an extra loop level; both keep two groups (deeper trips only cost
 // occupancy there).
-constexpr int sh_rows_per_trip(int ncm, int nv, int cw, bool seg) {
-    return (cw == 2 && !seg && (ncm <= 1 || nv == 0)) ? 6 : 2;
+constexpr int sh_rows_per_trip(int ncm, int nv, int cw, int rm) {
+    return (cw == 2 && rm != kRowsBlocksMulti && (ncm <= 1 || nv == 0)) ? 6 : 2;
 }
 
-template <int NCM, int NV, int CW, bool XVEC, bool SEG>
+// NCM MFMA column tiles (16 columns each) plus NV <= 8 columns on the vector
+// ALU, CW float4 column groups per lane (64 CW columns per wave). XVEC: the
+// vector-ALU columns are read as float4s (row pitch a multiple of 4 and all
+// NV columns inside the width). RM: how a split finds its rows (RowMode).
+template <int NCM, int NV, int CW, bool XVEC, int RM>
 __global__ __launch_bounds__(256) void sh_panel_kernel(const float* __restrict__ S, int64_t lds,
                                                        const float* __restrict__ X, int width,
                                                        RowPlan rp, int nsplit,
                                                        float* __restrict__ part, int ldp) {
-    constexpr int U = sh_rows_per_trip(NCM, NV, CW, SEG);
+    constexpr int U = sh_rows_per_trip(NCM, NV, CW, RM);
     constexpr int WCOLS = 64 * CW;    // columns per wave
     constexpr int NCM1 = NCM > 0 ? NCM : 1;
     constexpr int NV1 = NV > 0 ? NV : 1;
@@ -219,10 +223,10 @@ __global__ __launch_bounds__(256) void sh_panel_kernel(const float* __restrict__
         else run_rows(jb, je, std::true_type{});
     };
     int jb, je;
-    if (SEG) {
-        for (int g = 0; split_segment(rp, split, g, jb, je); ++g) run(jb, je);
+    if constexpr (RM == kRowsBlocksMulti) {
+        for (int g = 0; split_segment<RM>(rp, split, g, jb, je); ++g) run(jb, je);
     } else {
-        split_segment(rp, split, 0, jb, je);
+        split_segment<RM>(rp, split, 0, jb, je);
         run(jb, je);
     }
 
@@ -269,7 +273,7 @@ __global__ __launch_bounds__(256) void sh_panel_kernel(const float* __restrict__
         }
 }
 
-template <int NCM, int NV, int CW, bool SEG>
+template <int NCM, int NV, int CW, int RM>
 static hipError_t launch_sh_t(const float* S, int64_t lds, const float* X, int width,
                               const RowPlan& rp, int nsplit, float* part, int ldp, hipStream_t st) {
     const int ntiles = (rp.n + 256 * CW - 1) / (256 * CW);
@@ -277,10 +281,10 @@ static hipError_t launch_sh_t(const float* S, int64_t lds, const float* X, int w
     const bool xvec = NV > 0 && width % 4 == 0 && 16 * NCM + NV <= width &&
                       (reinterpret_cast<uintptr_t>(X) % 16) == 0;
     if (NV > 0 && xvec)
-        hipLaunchKernelGGL((sh_panel_kernel<NCM, NV, CW, (NV > 0), SEG>), grid, dim3(256), 0, st, S,
+        hipLaunchKernelGGL((sh_panel_kernel<NCM, NV, CW, (NV > 0), RM>), grid, dim3(256), 0, st, S,
                            lds, X, width, rp, nsplit, part, ldp);
     else
-        hipLaunchKernelGGL((sh_panel_kernel<NCM, NV, CW, false, SEG>), grid, dim3(256), 0, st, S,
+        hipLaunchKernelGGL((sh_panel_kernel<NCM, NV, CW, false, RM>), grid, dim3(256), 0, st, S,
                            lds, X, width, rp, nsplit, part, ldp);
     return hipGetLastError();
 }
@@ -289,11 +293,14 @@ template <int NCM, int NV, int CW>
 static hipError_t launch_sh_any(const float* S, int64_t lds, const float* X, int width,
                                 const RowPlan& rp, int nsplit, float* part, int ldp,
                                 hipStream_t st) {
-    // several row blocks per split: sampled passes of fit widths only (k <= 64)
-    const bool seg = rp.blocks != nullptr && rp.sub == 1 && rp.bps > 1;
-    if (!seg) return launch_sh_t<NCM, NV, CW, false>(S, lds, X, width, rp, nsplit, part, ldp, st);
-    if constexpr (16 * NCM + NV <= kMaxK)
-        return launch_sh_t<NCM, NV, CW, true>(S, lds, X, width, rp, nsplit, part, ldp, st);
+    if (rp.blocks == nullptr)
+        return launch_sh_t<NCM, NV, CW, kRowsContiguous>(S, lds, X, width, rp, nsplit, part, ldp, st);
+    // sampled row blocks: fit widths only (k <= 64)
+    if constexpr (16 * NCM + NV <= kMaxK) {
+        if (rp.sub == 1 && rp.bps > 1)
+            return launch_sh_t<NCM, NV, CW, kRowsBlocksMulti>(S, lds, X, width, rp, nsplit, part, ldp, st);
+        return launch_sh_t<NCM, NV, CW, kRowsBlocks>(S, lds, X, width, rp, nsplit, part, ldp, st);
+    }
     return hipErrorInvalidValue;
 }
 

@@ -140,6 +140,7 @@ FullPlan sampled_plan(int n, const int* blocks_dev, int nsel, int block_rows) {
         fp.nsplit = nsel * sub;
     } else {
         rp.sub = 1;
+        rp.seg = block_rows;  // read when one block per split remains (nsel == kMaxSplits)
         rp.bps = (int)cdiv(nsel, kMaxSplits);
         fp.nsplit = (int)cdiv(nsel, rp.bps);
     }

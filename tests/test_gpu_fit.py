@@ -236,20 +236,24 @@ def test_fit_deterministic(torch, api, c1):
     np.testing.assert_array_equal(a.f_trace, b.f_trace)
 
 
-def test_fit_block_svrg_multiblock_splits(torch, api):
-    """48 of 64 row blocks per sampled step: each split of the sampled pass
-    covers two blocks (the multi-block path of the S.H kernel)."""
+@pytest.mark.parametrize("phi0", [0.25, 0.5, 0.75])
+def test_fit_block_svrg_multiblock_splits(torch, api, phi0):
+    """16, 32 and 48 of 64 row blocks per sampled step. 16 and 32: one whole
+    block per split of the sampled pass (32 is the split cap, the boundary
+    between the two plans); 48: each split covers two blocks (the multi-block
+    path of the S.H kernel)."""
     w = synth.student_factor(n=4096, k=12, T=252, seed=5, min_size=64)
     S = oracle.abs_corr(w.X).astype(np.float32)
     S64 = S.astype(np.float64)
-    res = api.fit(S_to_dev(S, torch), w.k, solver="block_svrg", phi0=0.75, block_rows=64,
+    res = api.fit(S_to_dev(S, torch), w.k, solver="block_svrg", phi0=phi0, block_rows=64,
                   max_iters=60, tol_rel=0.0, seed=4)
     m = S64.mean()
     H0 = oracle.init_uniform(w.n, w.k, oracle.init_scale_matched(m, w.k), 4)
     ref = oracle.fit_adaptgrow(S64, H0, oracle.default_lr(m, w.k), 60,
-                               solver=oracle.SOLVER_BLOCK_SVRG, phi0=0.75, block_rows=64,
+                               solver=oracle.SOLVER_BLOCK_SVRG, phi0=phi0, block_rows=64,
                                tol=0.0, seed=4)
     assert res.report["n_blocks"] == 64 and res.report["start_branch"] == 1
+    assert res.report["doublings"] == len(ref["history"])
     fg, fr = np.asarray(res.f_trace), np.asarray(ref["f"])
     assert np.array_equal(np.isnan(fg), np.isnan(fr))
     ex = ~np.isnan(fr)
