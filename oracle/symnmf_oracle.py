@@ -25,6 +25,8 @@ that nothing outside this file can pin say "parity unpinned" below:
   parity unpinned for the constants; the structure is pinned by invariants.
 * ``fit_adaptgrow`` stagnation rule and phi seeding: parity unpinned (the
   pages name ``stagnating()`` and the seeding but do not define them).
+* ``calm_windows`` (which windows calibrate the 3-sigma limit) and the
+  warm start of ``rolling_fit``: readings of the pages, parity unpinned.
 """
 from __future__ import annotations
 
@@ -38,6 +40,7 @@ __all__ = [
     "default_lr", "sh_product", "objective_explicit", "objective_trace", "gradient",
     "adagrad_step", "fit_full", "sample_blocks", "svrg_sh_estimate",
     "gap_ratio", "initial_blocks", "fit_adaptgrow", "top_eigenvalues",
+    "ari_drift", "calm_windows", "control_limit", "cross_block_means", "rolling_fit",
     "labels", "ari", "ari_pairs", "SOLVER_AUTO", "SOLVER_FULL",
     "SOLVER_BLOCK_SVRG",
 ]
@@ -467,3 +470,97 @@ def ari_pairs(a, b):
     if mx == expected:
         return 1.0
     return (n11 - expected) / (mx - expected)
+
+
+# --------------------------------------------------------------------------
+# Re-clustering through time (P1 "Tracking stability through time with the
+# Rand index" and the tail/body discussion after it).
+# --------------------------------------------------------------------------
+
+
+def ari_drift(label_seq, delta):
+    """ARI(t - delta, t) of window t's hard labels against window t - delta's;
+    NaN for t < delta (no earlier window that far back)."""
+    W = len(label_seq)
+    out = np.full(W, np.nan)
+    for t in range(delta, W):
+        out[t] = ari(label_seq[t - delta], label_seq[t])
+    return out
+
+
+def calm_windows(W, T, delta, switch_day, stress_first, stress_last):
+    """Windows that calibrate the control limit: the pages calibrate on the
+    calm windows before the break. Reading: window t (days t .. t+T-1) is calm
+    when ARI(t - delta, t) exists, fewer than half of its days come after the
+    membership switch (so no switched label can have flipped yet) and it holds
+    no stressed day. Parity unpinned (the pages give no rule)."""
+    calm = np.zeros(W, dtype=bool)
+    for t in range(W):
+        after = max(0, t + T - switch_day)
+        stressed = not (t + T - 1 < stress_first or t > stress_last)
+        calm[t] = t >= delta and 2 * after < T and not stressed
+    return calm
+
+
+def control_limit(values, calm):
+    """The self-calibrating 3-sigma limit: mean minus three sample standard
+    deviations of the calm values; a value below it is flagged."""
+    v = np.asarray(values, dtype=np.float64)
+    c = v[np.asarray(calm, dtype=bool)]
+    mu = float(c.mean())
+    sd = float(c.std(ddof=1))
+    limit = mu - 3.0 * sd
+    flags = np.zeros(v.size, dtype=bool)
+    ok = ~np.isnan(v)
+    flags[ok] = v[ok] < limit
+    return limit, mu, sd, flags
+
+
+def cross_block_means(S, labels_, groups):
+    """m x m means of S over the blocks of the listed planted groups: entry
+    (a, b) is the mean of S_ij over i in group a and j in group b. The pages
+    track the off-diagonal (cross-sector) entries to see a co-crash."""
+    S = np.asarray(S, dtype=np.float64)
+    lab = np.asarray(labels_)
+    m = len(groups)
+    B = np.zeros((m, m))
+    for a in range(m):
+        ia = np.flatnonzero(lab == groups[a])
+        for b in range(m):
+            ib = np.flatnonzero(lab == groups[b])
+            B[a, b] = S[np.ix_(ia, ib)].mean()
+    return B
+
+
+def rolling_fit(X_stream, k, T, windows, kind="abscorr", iters=100, seed=0, warm_start=True,
+                tail=0.05, S_windows=None):
+    """Fit every window t = 0 .. windows-1 (days t .. t+T-1) with ``iters``
+    full-batch AdaGrad steps. The first window (every window without
+    warm_start) starts from the scale-matched seeded init; with warm_start a
+    window starts from the previous window's H with a fresh accumulator G
+    (a reading: the pages fit each window independently, the rolling
+    workload asks for a warm start; both are offered). lr is the default
+    reading per window. ``S_windows`` (optional) supplies each window's S
+    instead of building it (fit parity on the same fp32 S). Returns
+    per-window H, labels and objective traces."""
+    X_stream = np.asarray(X_stream)
+    Hs, labs, fs = [], [], []
+    H = None
+    for t in range(windows):
+        if S_windows is not None:
+            S = np.asarray(S_windows[t], dtype=np.float64)
+        else:
+            Xw = X_stream[t:t + T].astype(np.float32)
+            S = abs_corr(Xw) if kind == "abscorr" else tpdm(Xw, tail)
+            S = S.astype(np.float32).astype(np.float64)
+        m = S.mean()
+        if H is None or not warm_start:
+            H0 = init_uniform(S.shape[0], k, init_scale_matched(m, k), seed)
+        else:
+            H0 = H
+        out = fit_full(S, H0, default_lr(m, k), iters, tol=0.0)
+        H = out["H"]
+        Hs.append(H)
+        labs.append(labels(H))
+        fs.append(np.asarray(out["f"]))
+    return dict(H=Hs, labels=labs, f=fs)

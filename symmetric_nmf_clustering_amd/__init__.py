@@ -8,11 +8,11 @@ synthetic inputs.
 """
 from . import _lib  # noqa: F401
 
-__all__ = ["api", "synth", "metrics"]
+__all__ = ["api", "synth", "metrics", "rolling"]
 
 
 def __getattr__(name):
-    if name in ("api", "synth", "metrics"):
+    if name in ("api", "synth", "metrics", "rolling"):
         import importlib
 
         return importlib.import_module(f".{name}", __name__)

@@ -22,6 +22,14 @@ definitions this library is measured on:
   seeded group permutation receives an extra -5 (five unit standard
   deviations).
 
+* ``rolling_stream``: a D-day stream for rolling windows (the pages' "The
+  temporal setup": instruments change planted group, and several groups share
+  a tail-stress episode without changing group). Returns as in
+  ``student_factor``, day by day under the membership of that day: a seeded
+  fraction of instruments moves to another group from ``switch_day`` on, and
+  on days ``stress_first``..``stress_last`` (inclusive) every member of a
+  seeded set of groups receives an extra ``shock``.
+
 Draw order (numpy ``default_rng(seed)``) is fixed and documented per function,
 so a recipe is reproducible from its name, sizes and seed alone.
 """
@@ -129,6 +137,77 @@ def student_factor_stress(n: int = 8192, k: int = 24, T: int = 252,
                   "student_factor_stress", seed, meta)
 
 
+@dataclass
+class Stream:
+    """A D x n day-major return stream (float32) and its planted structure."""
+
+    X: np.ndarray
+    labels_before: np.ndarray   # membership before switch_day
+    labels_after: np.ndarray    # membership from switch_day on
+    switched: np.ndarray        # indices of the instruments that moved
+    k: int
+    switch_day: int
+    stress_groups: list
+    stress_first: int
+    stress_last: int            # inclusive
+    seed: int
+    meta: dict = field(default_factory=dict)
+
+    @property
+    def days(self) -> int:
+        return self.X.shape[0]
+
+    @property
+    def n(self) -> int:
+        return self.X.shape[1]
+
+    def window(self, t: int, T: int) -> np.ndarray:
+        """Days t .. t + T - 1 (a view)."""
+        if t < 0 or t + T > self.days:
+            raise ValueError("window outside the stream")
+        return self.X[t:t + T]
+
+
+def rolling_stream(n: int = 20000, k: int = 24, days: int = 501, switch_day: int = 300,
+                   switch_frac: float = 0.05, stress_groups: int = 3, stress_first: int = 420,
+                   stress_last: int = 430, shock: float = -5.0, seed: int = 5,
+                   min_size: int = 64) -> Stream:
+    """Student-t planted-factor stream with a membership switch and a co-crash.
+
+    Draw order: group sizes (multinomial), membership permutation (n),
+    loadings l (n), a permutation of the instruments (the first
+    round(switch_frac n) switch), for each switcher an offset in 1..k-1 (its new
+    group is (old + offset) mod k), a permutation of the k groups (the first
+    ``stress_groups`` are stressed), factors F (days x k), noise E (days x n).
+    The stressed groups are taken in the membership from ``switch_day`` on.
+    """
+    if not (0 <= switch_day <= days and 0 <= stress_first <= stress_last < days):
+        raise ValueError("event days outside the stream")
+    rng = np.random.default_rng(seed)
+    _, before = _student_groups(rng, n, k, min_size)
+    load = rng.uniform(0.3, 0.9, size=n)
+    nsw = int(round(switch_frac * n))
+    switched = np.sort(rng.permutation(n)[:nsw])
+    offs = rng.integers(1, k, size=nsw)
+    after = before.copy()
+    after[switched] = (before[switched] + offs) % k
+    gperm = rng.permutation(k)
+    groups = np.sort(gperm[:stress_groups])
+    F = _t4_unit(rng, (days, k))
+    E = _t4_unit(rng, (days, n))
+    X = np.empty((days, n), dtype=np.float64)
+    cut = switch_day
+    scale = np.sqrt(1.0 - load * load)
+    X[:cut] = load * F[:cut][:, before] + scale * E[:cut]
+    X[cut:] = load * F[cut:][:, after] + scale * E[cut:]
+    members = np.isin(after, groups)
+    X[stress_first:stress_last + 1, members] += shock
+    return Stream(np.ascontiguousarray(X, dtype=np.float32), before.astype(np.int32),
+                  after.astype(np.int32), switched, k, switch_day, groups.tolist(), stress_first,
+                  stress_last, seed, {"switch_frac": switch_frac, "shock": shock,
+                                      "min_size": min_size})
+
+
 # Named workloads: (recipe, kwargs).  The sizes are the ones the library is
 # measured and parity-tested on.
 WORKLOADS = {
@@ -138,6 +217,14 @@ WORKLOADS = {
                           dict(n=8192, k=24, T=252, seed=1)),
     "tfactor_n100000_k24": (student_factor,
                             dict(n=100000, k=24, T=252, seed=2)),
+}
+
+# The rolling workload: a 501-day stream read as 250 windows of 252 days.
+ROLLING = {
+    "rolling_n20000_k24": dict(stream=dict(n=20000, k=24, days=501, switch_day=300,
+                                           switch_frac=0.05, stress_groups=3, stress_first=420,
+                                           stress_last=430, seed=5),
+                               T=252, windows=250, iters=100, delta=50),
 }
 
 
