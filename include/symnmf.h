@@ -42,7 +42,7 @@ extern "C" {
 #endif
 #pragma GCC visibility push(default)
 
-#define SYMNMF_ABI_VERSION 1
+#define SYMNMF_ABI_VERSION 2
 
 enum symnmf_status {
     SYMNMF_OK = 0,
@@ -69,7 +69,13 @@ enum symnmf_init {
 };
 
 /* Operations for symnmf_workspace_bytes. */
-enum symnmf_op { SYMNMF_OP_BUILD_S = 0, SYMNMF_OP_PROBE = 1, SYMNMF_OP_FIT = 2, SYMNMF_OP_SH = 3 };
+enum symnmf_op {
+    SYMNMF_OP_BUILD_S = 0,
+    SYMNMF_OP_PROBE = 1,
+    SYMNMF_OP_FIT = 2,
+    SYMNMF_OP_SH = 3,
+    SYMNMF_OP_KMEANS = 4 /* k_or_p = k */
+};
 
 /* u(seed, c) above: the top 24 bits of output c+1 of SplitMix64 (Steele, Lea
  * and Flood, OOPSLA 2014) started at state `seed`, times 2^-24. */
@@ -207,6 +213,31 @@ int symnmf_fit(const float* S, int64_t n, int64_t lds, int32_t k,
  * Errors: E_INVALID, E_HIP. */
 int symnmf_labels(const float* H, int64_t n, int32_t k, int32_t* labels, void* hip_stream);
 
+/* Spherical k-means on the L2-normalised rows of S, the hard-clustering
+ * baseline (P1 "Spherical k-means for direct hard clustering": rows of S
+ * compared by cosine similarity; "Between spherical k-means and SymNMF").
+ * x_i = S[i,:] / ||S[i,:]||; the k initial centroids are the rows
+ * x_{r_0} < ... < x_{r_{k-1}} drawn without replacement by the Block-SVRG
+ * sampler's generator with this seed and step 0 (nb = n). Each iteration
+ * assigns every row to its most similar centroid (argmax_j <x_i, c_j>, lowest
+ * j on ties; computed as the row argmax of S C^T, S symmetric) and stops when
+ * no label changed; otherwise each centroid becomes the normalised sum of its
+ * rows (a cluster left empty keeps its centroid). Two passes over S per
+ * iteration.
+ * labels (n int32, device): the final assignment (made against the final
+ * centroids). centroids (nullable, device, n x k, ld k): column j holds c_j.
+ * iters_host (nullable): centroid updates made; converged_host (nullable): 1
+ * when the last assignment changed nothing; objective_host (nullable):
+ * sum_i <x_i, c_{labels[i]}> of the final assignment (fp64).
+ * Requires S symmetric, 1 <= k <= 64, k <= n, max_iters >= 0.
+ * Returns OK, W_NOT_CONVERGED (max_iters updates made and the last assignment
+ * still moved rows), or E_INVALID / E_WORKSPACE / E_HIP. */
+int symnmf_spherical_kmeans(const float* S, int64_t n, int64_t lds, int32_t k,
+                            int32_t max_iters, uint64_t seed, int32_t* labels,
+                            float* centroids, int32_t* iters_host,
+                            int32_t* converged_host, double* objective_host,
+                            void* ws, size_t ws_bytes, void* hip_stream);
+
 const char* symnmf_status_string(int status);
 int symnmf_abi_version(void);
 
@@ -221,7 +252,8 @@ enum symnmf_prof_kernel {
     SYMNMF_PROF_SH_PROBE = 2,   /* the probe's S.Q pass                        */
     SYMNMF_PROF_BUILD_GRAM = 3, /* the MFMA Z^T Z / Theta^T Theta build        */
     SYMNMF_PROF_UPDATE = 4,     /* fused reduce + gradient + AdaGrad + Gram    */
-    SYMNMF_PROF_COUNT = 5
+    SYMNMF_PROF_SH_KMEANS = 5,  /* the spherical k-means passes over S         */
+    SYMNMF_PROF_COUNT = 6
 };
 void symnmf_profile_enable(int on);
 void symnmf_profile_reset(void);

@@ -41,6 +41,7 @@ __all__ = [
     "adagrad_step", "fit_full", "sample_blocks", "svrg_sh_estimate",
     "gap_ratio", "initial_blocks", "fit_adaptgrow", "top_eigenvalues",
     "ari_drift", "calm_windows", "control_limit", "cross_block_means", "rolling_fit",
+    "spherical_kmeans", "boundary_fraction",
     "labels", "ari", "ari_pairs", "SOLVER_AUTO", "SOLVER_FULL",
     "SOLVER_BLOCK_SVRG",
 ]
@@ -564,3 +565,58 @@ def rolling_fit(X_stream, k, T, windows, kind="abscorr", iters=100, seed=0, warm
         labs.append(labels(H))
         fs.append(np.asarray(out["f"]))
     return dict(H=Hs, labels=labs, f=fs)
+
+
+# --------------------------------------------------------------------------
+# Spherical k-means, the hard-clustering baseline (P1 "Spherical k-means for
+# direct hard clustering", "Between spherical k-means and SymNMF").
+# --------------------------------------------------------------------------
+
+
+def spherical_kmeans(S, k, max_iters=100, seed=0):
+    """Spherical k-means (Dhillon and Modha 2001) on the rows of S scaled to
+    unit length, similarity = cosine. Initial centroids: the rows drawn by
+    ``sample_blocks(seed, 0, n, k)`` (ascending). Each iteration assigns every
+    row to its most similar centroid (lowest index on ties) and stops when no
+    label changed; otherwise every centroid becomes the normalised sum of its
+    rows (an empty cluster keeps its centroid). ``iters`` counts the centroid
+    updates; ``objective`` is the summed similarity of the final assignment."""
+    S = np.asarray(S, dtype=np.float64)
+    n = S.shape[0]
+    r = np.sqrt((S * S).sum(axis=1))
+    X = np.zeros_like(S)
+    nz = r > 0
+    X[nz] = S[nz] / r[nz, None]
+    C = X[sample_blocks(seed, 0, n, k)].copy()
+    labels_ = np.full(n, k)
+    updates = 0
+    converged = False
+    while True:
+        sims = X @ C.T
+        new = np.argmax(sims, axis=1)
+        obj = float(sims[np.arange(n), new].sum())
+        changed = int((new != labels_).sum())
+        labels_ = new
+        if changed == 0:
+            converged = True
+            break
+        if updates >= max_iters:
+            break
+        for j in range(k):
+            s_j = X[labels_ == j].sum(axis=0)
+            norm = np.linalg.norm(s_j)
+            if norm > 0:
+                C[j] = s_j / norm
+        updates += 1
+    return dict(labels=labels_.astype(np.int32), C=C, iters=updates, converged=converged,
+                objective=obj)
+
+
+def boundary_fraction(H, ratio=0.5):
+    """Share of rows whose second-largest loading is at least ``ratio`` times
+    their largest (rows split across two clusters; an all-zero row is not
+    counted). Reading: the pages count "boundary" instruments whose soft
+    loadings stay split but give no rule; parity unpinned."""
+    H = np.asarray(H, dtype=np.float64)
+    top2 = np.sort(H, axis=1)[:, -2:]
+    return float(np.mean((top2[:, 1] > 0) & (top2[:, 0] >= ratio * top2[:, 1])))

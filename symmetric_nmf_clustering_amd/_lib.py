@@ -23,11 +23,12 @@ E_DEGENERATE = -5
 ABSCORR, TPDM = 0, 1
 AUTO, FULL, BLOCK_SVRG = 0, 1, 2
 INIT_UNIFORM, INIT_SCALE_MATCHED, INIT_CALLER = 0, 1, 2
-OP_BUILD_S, OP_PROBE, OP_FIT, OP_SH = 0, 1, 2, 3
-PROF_SH_FULL, PROF_SH_SAMPLED, PROF_SH_PROBE, PROF_BUILD_GRAM, PROF_UPDATE = 0, 1, 2, 3, 4
+OP_BUILD_S, OP_PROBE, OP_FIT, OP_SH, OP_KMEANS = 0, 1, 2, 3, 4
+(PROF_SH_FULL, PROF_SH_SAMPLED, PROF_SH_PROBE, PROF_BUILD_GRAM, PROF_UPDATE,
+ PROF_SH_KMEANS) = 0, 1, 2, 3, 4, 5
 PROF_NAMES = {
     PROF_SH_FULL: "sh_full", PROF_SH_SAMPLED: "sh_sampled", PROF_SH_PROBE: "sh_probe",
-    PROF_BUILD_GRAM: "build_gram", PROF_UPDATE: "update",
+    PROF_BUILD_GRAM: "build_gram", PROF_UPDATE: "update", PROF_SH_KMEANS: "sh_kmeans",
 }
 
 
@@ -99,6 +100,9 @@ SIGNATURES = [
       _P, _P, ctypes.POINTER(_D), _I32, ctypes.POINTER(FitReport), _P,
       ctypes.c_size_t, _P]),
     ("symnmf_labels", ctypes.c_int, [_P, _I64, _I32, _P, _P]),
+    ("symnmf_spherical_kmeans", ctypes.c_int,
+     [_P, _I64, _I64, _I32, _I32, ctypes.c_uint64, _P, _P, ctypes.POINTER(_I32),
+      ctypes.POINTER(_I32), ctypes.POINTER(_D), _P, ctypes.c_size_t, _P]),
     ("symnmf_profile_enable", None, [ctypes.c_int]),
     ("symnmf_profile_reset", None, []),
     ("symnmf_profile_read", ctypes.c_int,

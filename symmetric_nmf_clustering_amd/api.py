@@ -214,6 +214,36 @@ def labels(H: torch.Tensor) -> torch.Tensor:
     return out
 
 
+@dataclass
+class KmeansResult:
+    labels: torch.Tensor
+    centroids: Optional[torch.Tensor]
+    iterations: int
+    converged: bool
+    objective: float
+    status: int
+
+
+def spherical_kmeans(S: torch.Tensor, k: int, *, max_iters: int = 100, seed: int = 0,
+                     return_centroids: bool = False) -> KmeansResult:
+    """Spherical k-means on the L2-normalised rows of S (the hard-clustering
+    baseline). Returns labels (n int32), optionally the centroids (n x k, column
+    j = centroid j), the number of centroid updates, whether the last
+    assignment moved no row, and sum_i <x_i, c_label(i)>."""
+    n, lds = _S_layout(S)
+    lab = torch.empty(n, dtype=torch.int32, device=S.device)
+    C = torch.empty((n, k), dtype=torch.float32, device=S.device) if return_centroids else None
+    ws = workspace(workspace_bytes(L.OP_KMEANS, n, k), S.device)
+    it = ctypes.c_int32(0)
+    conv = ctypes.c_int32(0)
+    obj = ctypes.c_double(0.0)
+    st = L.load().symnmf_spherical_kmeans(_ptr(S), n, lds, k, max_iters, seed, _ptr(lab), _ptr(C),
+                                          ctypes.byref(it), ctypes.byref(conv), ctypes.byref(obj),
+                                          _ptr(ws), ws.numel(), ctypes.c_void_p(_stream_ptr()))
+    L.check(st, "symnmf_spherical_kmeans")
+    return KmeansResult(lab, C, it.value, bool(conv.value), obj.value, st)
+
+
 # ---- kernel timing ---------------------------------------------------------
 def profile_enable(on: bool = True):
     L.load().symnmf_profile_enable(1 if on else 0)

@@ -103,6 +103,26 @@ hipError_t launch_finalize(FitDev* fd, double* f_trace, int t, int nblk, int k,
 hipError_t launch_count_zero_rows(const float* H, int n, int k, int* out, hipStream_t st);
 hipError_t launch_labels(const float* H, int64_t n, int k, int32_t* labels, hipStream_t st);
 
+// ---- spherical k-means (k_kmeans.hip) -----------------------------------------
+// rinv[i] = 1/||S[i,:]||_2 (fp64 sum of squares; 0 for a zero row).
+hipError_t launch_row_norm_inv(const float* S, int64_t lds, int n, float* rinv, hipStream_t st);
+// Ct[l][j] = S[idx[j]][l] * rinv[idx[j]] (n x k, ld k).
+hipError_t launch_gather_centroids(const float* S, int64_t lds, int n, const int* idx,
+                                   const float* rinv, int k, float* Ct, hipStream_t st);
+// *changes += #{i : lab[i] != lab_prev[i]}; obj_part[b] = sum over rows of
+// block b (256 rows) of rinv[i] * P[i][lab[i]] (fp64).
+hipError_t launch_kmeans_assign_stats(const float* P, int n, int k, const int32_t* lab,
+                                      const int32_t* lab_prev, const float* rinv, int* changes,
+                                      double* obj_part, hipStream_t st);
+// W[i][j] = lab[i] == j ? rinv[i] : 0.
+hipError_t launch_onehot_scaled(const int32_t* lab, const float* rinv, int n, int k, float* W,
+                                hipStream_t st);
+// Ct[:, j] = C[:, j] / ||C[:, j]|| where that norm is > 0 (else Ct[:, j] kept);
+// part: ceil(n/256) * k doubles, norm: k doubles.
+hipError_t launch_normalize_columns(const float* C, int n, int k, double* part, double* norm,
+                                    float* Ct, hipStream_t st);
+hipError_t launch_fill_int(int32_t* p, int64_t count, int32_t v, hipStream_t st);
+
 // ---- probe helpers ----------------------------------------------------------
 // C = A^T B (w x w, fp64) for n x w matrices A, B (ld w): per-block fp32
 // partials, then a fixed-order fp64 reduction into C.

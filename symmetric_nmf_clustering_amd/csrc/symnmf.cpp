@@ -248,6 +248,32 @@ size_t sh_layout(void* ws, int64_t n, int width, ShLayout* L) {
     return c.off;
 }
 
+struct KmeansLayout {
+    float *rinv, *Ct, *W, *C, *part;
+    int32_t *lab[2], *idx, *changes;
+    double *obj_part, *obj, *col_part, *norm;
+};
+size_t kmeans_layout(void* ws, int64_t n, int k, KmeansLayout* L) {
+    Carve c(ws);
+    FullPlan fp = full_plan((int)n);
+    const int64_t nblk = cdiv(n, 256);
+    KmeansLayout l;
+    l.rinv = c.take<float>((size_t)n);
+    l.Ct = c.take<float>((size_t)n * k);
+    l.W = c.take<float>((size_t)n * k);
+    l.C = c.take<float>((size_t)n * k);
+    l.part = c.take<float>((size_t)fp.nsplit * n * ldp_of(k));
+    for (int i = 0; i < 2; ++i) l.lab[i] = c.take<int32_t>((size_t)n);
+    l.idx = c.take<int32_t>((size_t)k);
+    l.changes = c.take<int32_t>(1);
+    l.obj_part = c.take<double>((size_t)nblk);
+    l.obj = c.take<double>(1);
+    l.col_part = c.take<double>((size_t)nblk * k);
+    l.norm = c.take<double>((size_t)k);
+    if (L) *L = l;
+    return c.off;
+}
+
 struct ProbeLayout {
     float *Q, *Y, *part, *M, *cg_part;
     double* C;
@@ -381,6 +407,9 @@ size_t symnmf_workspace_bytes(int op, int64_t n, int32_t k_or_p, int64_t T,
         case SYMNMF_OP_SH:
             if (k_or_p < 1 || k_or_p > kMaxWidth) return 0;
             return sh_layout(nullptr, n, k_or_p, nullptr);
+        case SYMNMF_OP_KMEANS:
+            if (k_or_p < 1 || k_or_p > kMaxK || k_or_p > n) return 0;
+            return kmeans_layout(nullptr, n, k_or_p, nullptr);
         case SYMNMF_OP_FIT: {
             if (k_or_p < 1 || k_or_p > kMaxK) return 0;
             symnmf_fit_params d;
@@ -911,6 +940,86 @@ int symnmf_fit(const float* S, int64_t n, int64_t lds, int32_t k, const symnmf_f
     }
     if (converged || P.tol_rel == 0.0) return SYMNMF_OK;
     return SYMNMF_W_NOT_CONVERGED;
+}
+
+// ---------------------------------------------------------------------------
+// Spherical k-means (P1 "Spherical k-means for direct hard clustering").
+int symnmf_spherical_kmeans(const float* S, int64_t n, int64_t lds, int32_t k,
+                            int32_t max_iters, uint64_t seed, int32_t* labels,
+                            float* centroids, int32_t* iters_host, int32_t* converged_host,
+                            double* objective_host, void* ws, size_t ws_bytes,
+                            void* hip_stream) {
+    if (!S || !labels || n < 1 || n > INT32_MAX / 2 || k < 1 || k > kMaxK || k > n ||
+        max_iters < 0 || lds < n || lds % 4 || !aligned(S, 16) || !aligned(labels, 4) ||
+        (centroids && !aligned(centroids, 4)))
+        return SYMNMF_E_INVALID;
+    const size_t need = kmeans_layout(nullptr, n, k, nullptr);
+    if (!ws_ok(ws, ws_bytes, need)) return SYMNMF_E_WORKSPACE;
+    KmeansLayout L;
+    kmeans_layout(ws, n, k, &L);
+    hipStream_t st = as_stream(hip_stream);
+    const int nn = (int)n;
+    const FullPlan fp = full_plan(nn);
+    const int ldp = ldp_of(k);
+    const double pass_bytes = 4.0 * n * (double)n + 8.0 * (double)n * k;
+    const int64_t nblk = cdiv(n, 256);
+
+    // x_i = S[i,:] / ||S[i,:]||; the seeded initial rows become the centroids
+    HIPCHK(launch_row_norm_inv(S, lds, nn, L.rinv, st));
+    {
+        std::vector<int> perm, idx(k);
+        sample_blocks(seed, 0, nn, k, perm, idx.data());
+        HIPCHK(hipMemcpyAsync(L.idx, idx.data(), sizeof(int) * k, hipMemcpyHostToDevice, st));
+        HIPCHK(launch_gather_centroids(S, lds, nn, L.idx, L.rinv, k, L.Ct, st));
+        HIPCHK(hipStreamSynchronize(st));  // idx lives on the host stack
+    }
+    // labels before the first assignment: k, which no assignment produces
+    HIPCHK(launch_fill_int(L.lab[0], n, k, st));
+    int cur = 0;  // lab[cur]: labels of the last assignment
+    int updates = 0, changes = 0;
+    bool converged = false;
+    double obj = 0.0;
+    for (;;) {
+        // assignment: the row argmax of S C^T
+        {
+            ProfScope ps(SYMNMF_PROF_SH_KMEANS, pass_bytes, st);
+            HIPCHK(launch_sh_panel(S, lds, L.Ct, k, fp.rp, fp.nsplit, L.part, ldp, st));
+        }
+        HIPCHK(launch_reduce_partials(L.part, fp.nsplit, nn, k, ldp, L.C, nullptr, nullptr, st));
+        int32_t* lab_new = L.lab[cur ^ 1];
+        HIPCHK(launch_labels(L.C, n, k, lab_new, st));
+        HIPCHK(launch_fill_int(L.changes, 1, 0, st));
+        HIPCHK(launch_kmeans_assign_stats(L.C, nn, k, lab_new, L.lab[cur], L.rinv, L.changes,
+                                          L.obj_part, st));
+        HIPCHK(launch_sum_doubles(L.obj_part, nblk, L.obj, st));
+        HIPCHK(hipMemcpyAsync(&changes, L.changes, sizeof(int), hipMemcpyDeviceToHost, st));
+        HIPCHK(hipMemcpyAsync(&obj, L.obj, sizeof(double), hipMemcpyDeviceToHost, st));
+        HIPCHK(hipStreamSynchronize(st));
+        cur ^= 1;
+        if (!std::isfinite(obj)) return SYMNMF_E_NONFINITE;
+        if (changes == 0) {
+            converged = true;
+            break;
+        }
+        if (updates >= max_iters) break;
+        // update: C^T = normalise(S D^-1 Z), empty clusters keep their centroid
+        HIPCHK(launch_onehot_scaled(L.lab[cur], L.rinv, nn, k, L.W, st));
+        {
+            ProfScope ps(SYMNMF_PROF_SH_KMEANS, pass_bytes, st);
+            HIPCHK(launch_sh_panel(S, lds, L.W, k, fp.rp, fp.nsplit, L.part, ldp, st));
+        }
+        HIPCHK(launch_reduce_partials(L.part, fp.nsplit, nn, k, ldp, L.C, nullptr, nullptr, st));
+        HIPCHK(launch_normalize_columns(L.C, nn, k, L.col_part, L.norm, L.Ct, st));
+        ++updates;
+    }
+    HIPCHK(hipMemcpyAsync(labels, L.lab[cur], sizeof(int32_t) * n, hipMemcpyDeviceToDevice, st));
+    if (centroids)
+        HIPCHK(hipMemcpyAsync(centroids, L.Ct, sizeof(float) * n * k, hipMemcpyDeviceToDevice, st));
+    HIPCHK(hipStreamSynchronize(st));
+    if (iters_host) *iters_host = updates;
+    if (converged_host) *converged_host = converged ? 1 : 0;
+    if (objective_host) *objective_host = obj;
+    return converged ? SYMNMF_OK : SYMNMF_W_NOT_CONVERGED;
 }
 
 }  // extern "C"

@@ -39,7 +39,7 @@ def test_every_declared_symbol_is_exported():
 
 def test_abi_version_and_status_strings():
     lib = L.load()
-    assert lib.symnmf_abi_version() == 1
+    assert lib.symnmf_abi_version() == 2
     for s in (0, 1, -1, -2, -3, -4, -5):
         assert len(L.status_string(s)) > 0
     assert L.status_string(12345) == "unknown status"
@@ -92,6 +92,8 @@ def test_workspace_is_order_nk(golden_dir):
         assert 0 < sh < 40 * n * k * 4 + 2 ** 20   # <= 32 split partials of n x k
         probe = lib.symnmf_workspace_bytes(L.OP_PROBE, n, 64, 0, None)
         assert 0 < probe < 40 * n * 80 * 4 + 2 ** 22
+        km = lib.symnmf_workspace_bytes(L.OP_KMEANS, n, k, 0, None)
+        assert 0 < km < 40 * n * k * 4 + 2 ** 20
     # peak device storage of a fit at n = 1e5: the S itself (4 n^2) plus
     # workspace well under 1% of it (the pages' ~4 n^2 bytes)
     n = 100000
@@ -101,6 +103,8 @@ def test_workspace_is_order_nk(golden_dir):
     assert lib.symnmf_workspace_bytes(L.OP_PROBE, n, 113, 0, None) == 0  # w > 128
     assert lib.symnmf_workspace_bytes(L.OP_BUILD_S, n, 1, 1, None) == 0  # T < 2
     assert lib.symnmf_workspace_bytes(99, n, 1, 1, None) == 0
+    assert lib.symnmf_workspace_bytes(L.OP_KMEANS, n, 65, 0, None) == 0   # k > 64
+    assert lib.symnmf_workspace_bytes(L.OP_KMEANS, 10, 11, 0, None) == 0  # k > n
 
 
 FAKE = ctypes.c_void_p(0x10000)  # never dereferenced: every call below fails validation
@@ -127,6 +131,15 @@ def test_invalid_arguments_rejected_before_device_work():
     assert lib.symnmf_sh(FAKE, 100, 98, FAKE, 8, P, None, FAKE, z, None) == L.E_INVALID
     assert lib.symnmf_labels(None, 10, 3, FAKE, None) == L.E_INVALID
     assert lib.symnmf_labels(FAKE, 0, 3, FAKE, None) == L.OK  # empty input: nothing to do
+    km = lib.symnmf_spherical_kmeans
+    assert km(None, 100, 100, 4, 10, 0, FAKE, None, None, None, None, FAKE, z, None) == L.E_INVALID
+    assert km(FAKE, 100, 100, 4, 10, 0, None, None, None, None, None, FAKE, z, None) == L.E_INVALID
+    assert km(FAKE, 100, 100, 0, 10, 0, FAKE, None, None, None, None, FAKE, z, None) == L.E_INVALID
+    assert km(FAKE, 100, 100, 65, 10, 0, FAKE, None, None, None, None, FAKE, z, None) == L.E_INVALID
+    assert km(FAKE, 3, 4, 4, 10, 0, FAKE, None, None, None, None, FAKE, z, None) == L.E_INVALID  # k > n
+    assert km(FAKE, 100, 100, 4, -1, 0, FAKE, None, None, None, None, FAKE, z, None) == L.E_INVALID
+    assert km(FAKE, 100, 102, 4, 10, 0, FAKE, None, None, None, None, FAKE, z, None) == L.E_INVALID  # lds % 4
+    assert km(FAKE, 100, 100, 4, 10, 0, FAKE, None, None, None, None, FAKE, 64, None) == L.E_WORKSPACE
 
 
 def test_fit_argument_validation():

@@ -92,3 +92,22 @@ def test_fullsize_labels_property(big):
     first = np.argmax(H == mx[:, None], axis=1)
     assert np.array_equal(first, lab)
     assert res.H.min().item() >= 0.0
+
+
+def test_fullsize_spherical_kmeans(big):
+    """Spherical k-means at n = 100 000 in the benchmark's S: converges, the
+    labels are the row argmax of S C^T against the returned centroids on
+    sampled rows (recomputed in fp64 from the returns), and the planted groups
+    are found up to a few merged ones."""
+    torch, api, w, S, fro, rows = big
+    res = api.spherical_kmeans(S, K, seed=0, return_centroids=True)
+    assert res.converged
+    lab = res.labels.cpu().numpy()
+    C = res.centroids.cpu().numpy().astype(np.float64)
+    S_rows = oracle.abs_corr_rows(w.X, rows)
+    sims = S_rows @ C
+    best = sims.max(axis=1)
+    # the chosen centroid is the most similar one up to fp32 noise of S C^T
+    assert np.all(sims[np.arange(rows.size), lab[rows]] >= best - 1e-5 * np.abs(best))
+    # a local optimum from k seeded random rows (measured ARI 0.89)
+    assert oracle.ari(lab, w.labels) >= 0.8

@@ -128,3 +128,57 @@ def test_library_calm_mask_and_limit_match_oracle(W, T, delta, sw, s0, s1):
         ref = oracle.control_limit(v, calm)
         assert got[0] == pytest.approx(ref[0], rel=1e-14)
         np.testing.assert_array_equal(got[3], ref[3])
+
+
+# ---- spherical k-means (P1 "Spherical k-means for direct hard clustering") ----
+
+def test_kmeans_recovers_noise_free_blocks():
+    """S = blockdiag(1 1^T): rows of one block are identical unit vectors, so
+    with one initial row per block the first assignment is already the planted
+    partition and the run stops after one update."""
+    k, size = 4, 16
+    truth = np.repeat(np.arange(k), size)
+    S = (truth[:, None] == truth[None, :]).astype(np.float64)
+    seed = next(s for s in range(100)
+                if len(set(truth[oracle.sample_blocks(s, 0, k * size, k)])) == k)
+    out = oracle.spherical_kmeans(S, k, seed=seed)
+    assert out["converged"] and out["iters"] == 1
+    assert oracle.ari(out["labels"], truth) == 1.0
+    # each row has similarity 1 with its own block's centroid
+    assert out["objective"] == pytest.approx(k * size, rel=1e-14)
+
+
+def test_kmeans_objective_closed_form_and_monotone():
+    rng = np.random.default_rng(4)
+    A = rng.random((60, 60)) ** 3
+    S = (A + A.T) / 2
+    out = oracle.spherical_kmeans(S, 5, seed=1)
+    assert out["converged"]
+    # at a fixed point c_j = s_j / ||s_j||, so sum_i <x_i, c_l(i)> = sum_j ||s_j||
+    X = S / np.linalg.norm(S, axis=1, keepdims=True)
+    lab = out["labels"]
+    closed = sum(np.linalg.norm(X[lab == j].sum(axis=0)) for j in range(5))
+    assert out["objective"] == pytest.approx(closed, rel=1e-12)
+    # and every row sits with its most similar centroid
+    sims = X @ out["C"].T
+    assert np.all(sims[np.arange(60), lab] >= sims.max(axis=1) - 1e-12)
+    # the summed similarity never falls from one iteration to the next
+    objs = [oracle.spherical_kmeans(S, 5, max_iters=m, seed=1)["objective"] for m in range(out["iters"] + 1)]
+    assert all(b >= a - 1e-12 for a, b in zip(objs, objs[1:]))
+
+
+def test_kmeans_initial_rows_are_the_documented_draw():
+    rng = np.random.default_rng(5)
+    A = rng.random((40, 40))
+    S = (A + A.T) / 2
+    out = oracle.spherical_kmeans(S, 3, max_iters=0, seed=9)
+    rows = oracle.sample_blocks(9, 0, 40, 3)
+    X = S / np.linalg.norm(S, axis=1, keepdims=True)
+    np.testing.assert_array_equal(out["C"], X[rows])
+    np.testing.assert_array_equal(out["labels"], np.argmax(X @ X[rows].T, axis=1))
+
+
+def test_boundary_fraction_hand_case():
+    # ratios of second to first loading: 0, 0.6, 0.4, (zero row), 0.49, 0.5
+    H = np.array([[1.0, 0.0], [1.0, 0.6], [0.4, 1.0], [0.0, 0.0], [1.0, 0.49], [0.5, 1.0]])
+    assert oracle.boundary_fraction(H) == pytest.approx(2 / 6)
