@@ -24,6 +24,9 @@ Readings (the pages leave these open):
   to convergence (relative change below ``first_tol``, at most
   ``first_max_iters`` steps): otherwise the first windows of the series would be
   compared against a fit that had only ``iters`` steps.
+* boundary instruments: rows of H whose second-largest loading is at least
+  half the largest (the pages count instruments that the soft factorization
+  keeps split across two clusters but give no rule).
 * cross-sector dependence: the mean of S_ij over pairs i, j in different
   monitored groups, raw and scaled to S_ij / sqrt(S_ii S_jj) (the raw TPDM is
   of order 1/n, the scaled one is comparable with |corr|, whose diagonal is 1).
@@ -71,11 +74,15 @@ def three_sigma(values: np.ndarray, calm: np.ndarray):
 def run(stream, *, T: int, windows: int, k: int, iters: int = 100, delta: int = 50,
         kinds=KINDS, warm_start: bool = True, seed: int = 0, tail_frac: float = 0.05,
         monitor_groups=None, keep_H: bool = False, first_max_iters: int = 2000,
-        first_tol: float = 1e-6) -> dict:
+        first_tol: float = 1e-6, kmeans: bool = False, kmeans_iters: int = 100,
+        boundary_ratio: float = 0.5) -> dict:
     """Run the rolling workload on ``cuda:0``; returns a dict of per-kind results.
 
     ``stream`` is a ``synth.Stream`` (host); its returns are copied to the device
-    once and every window is a view of that copy."""
+    once and every window is a view of that copy. With ``kmeans`` every window
+    also gets the spherical k-means baseline on the same S (seeded the same in
+    every window), its agreement with the SymNMF labels, and the share of
+    boundary instruments in H."""
     import torch
 
     from . import api, metrics
@@ -104,6 +111,10 @@ def run(stream, *, T: int, windows: int, k: int, iters: int = 100, delta: int = 
         t_build = np.empty(windows)
         t_fit = np.empty(windows)
         t_mon = np.empty(windows)
+        t_km = np.zeros(windows)
+        km_ari = np.full(windows, np.nan)
+        km_iters = np.zeros(windows, dtype=np.int32)
+        boundary = np.empty(windows)
         Hs = []
         H = None
         torch.cuda.synchronize()
@@ -132,14 +143,23 @@ def run(stream, *, T: int, windows: int, k: int, iters: int = 100, delta: int = 
             Pm = P.cpu().numpy().astype(np.float64)
             Pnm = Pn.cpu().numpy().astype(np.float64)
             d_host = dg.cpu().numpy()
+            Hh = H.cpu().numpy()
             c3 = time.perf_counter()
+            top2 = np.sort(Hh, axis=1)[:, -2:]
+            boundary[t] = float(np.mean((top2[:, 1] > 0) & (top2[:, 0] >= boundary_ratio * top2[:, 1])))
+            if kmeans:
+                km = api.spherical_kmeans(S, k, max_iters=kmeans_iters, seed=seed)
+                km_lab = km.labels.cpu().numpy()
+                t_km[t] = time.perf_counter() - c3
+                km_iters[t] = km.iterations
+                km_ari[t] = metrics.adjusted_rand_index(km_lab, labs[t])
             block[t] = (member.astype(np.float64).T @ Pm) / np.outer(sizes, sizes)
             block_n[t] = ((member.astype(np.float64) * d_host[:, None]).T @ Pnm) / np.outer(sizes, sizes)
             f_first[t] = res.f_trace[0]
             f_last[t] = res.f_trace[-1]
             t_build[t], t_fit[t], t_mon[t] = c1 - c0, c2 - c1, c3 - c2
             if keep_H:
-                Hs.append(H.cpu().numpy())
+                Hs.append(Hh)
         drift = np.full(windows, np.nan)
         for t in range(delta, windows):
             drift[t] = metrics.adjusted_rand_index(labs[t - delta], labs[t])
@@ -158,7 +178,9 @@ def run(stream, *, T: int, windows: int, k: int, iters: int = 100, delta: int = 
              "ari_drift": drift, "limit": limit, "calm_mean": mean,
              "calm_sd": sd, "flags": flags, "ari_vs_before": planted_before,
              "ari_vs_after": planted_after, "build_s": t_build, "fit_s": t_fit,
-             "monitor_s": t_mon}
+             "monitor_s": t_mon, "boundary_fraction": boundary}
+        if kmeans:
+            r.update({"kmeans_s": t_km, "kmeans_iters": km_iters, "kmeans_vs_symnmf_ari": km_ari})
         if keep_H:
             r["H"] = Hs
         out["kinds"][kind] = r
@@ -195,7 +217,14 @@ def summary(res: dict, stream) -> dict:
                 float(r["cross_dependence_scaled"][holds_stress].max()) if holds_stress.any() else None,
             "ari_vs_planted_first_window": float(r["ari_vs_before"][0]),
             "ari_vs_planted_last_window": float(r["ari_vs_after"][-1]),
+            "boundary_fraction_mean": float(r["boundary_fraction"].mean()),
         }
+        if "kmeans_s" in r:
+            d["kinds"][kind].update({
+                "kmeans_ms_mean": 1e3 * float(r["kmeans_s"].mean()),
+                "kmeans_iters_mean": float(r["kmeans_iters"].mean()),
+                "kmeans_vs_symnmf_ari_mean": float(np.nanmean(r["kmeans_vs_symnmf_ari"])),
+            })
     return d
 
 
@@ -207,12 +236,13 @@ def main(argv=None):
     ap.add_argument("--windows", type=int, default=None)
     ap.add_argument("--cold", action="store_true", help="fit every window from the seeded init")
     ap.add_argument("--save", default=None, help="write the per-window series to this .npz")
+    ap.add_argument("--no-kmeans", action="store_true", help="skip the spherical k-means baseline")
     args = ap.parse_args(argv)
     cfg = synth.ROLLING[args.workload]
     stream = synth.rolling_stream(**cfg["stream"])
     W = cfg["windows"] if args.windows is None else args.windows
     res = run(stream, T=cfg["T"], windows=W, k=cfg["stream"]["k"], iters=cfg["iters"],
-              delta=cfg["delta"], warm_start=not args.cold)
+              delta=cfg["delta"], warm_start=not args.cold, kmeans=not args.no_kmeans)
     if args.save:
         arrays = {f"{kind}_{key}": np.asarray(val) for kind, r in res["kinds"].items()
                   for key, val in r.items() if key not in ("labels", "H")}
