@@ -534,7 +534,7 @@ def cross_block_means(S, labels_, groups):
 
 
 def rolling_fit(X_stream, k, T, windows, kind="abscorr", iters=100, seed=0, warm_start=True,
-                tail=0.05, S_windows=None):
+                tail=0.05, S_windows=None, first_max_iters=None, first_tol=1e-6):
     """Fit every window t = 0 .. windows-1 (days t .. t+T-1) with ``iters``
     full-batch AdaGrad steps. The first window (every window without
     warm_start) starts from the scale-matched seeded init; with warm_start a
@@ -542,7 +542,9 @@ def rolling_fit(X_stream, k, T, windows, kind="abscorr", iters=100, seed=0, warm
     (a reading: the pages fit each window independently, the rolling
     workload asks for a warm start; both are offered). lr is the default
     reading per window. ``S_windows`` (optional) supplies each window's S
-    instead of building it (fit parity on the same fp32 S). Returns
+    instead of building it. With warm_start and ``first_max_iters`` the first
+    window runs to convergence (relative change below ``first_tol``, at most
+    ``first_max_iters`` steps), the later ones ``iters`` steps. Returns
     per-window H, labels and objective traces."""
     X_stream = np.asarray(X_stream)
     Hs, labs, fs = [], [], []
@@ -559,7 +561,10 @@ def rolling_fit(X_stream, k, T, windows, kind="abscorr", iters=100, seed=0, warm
             H0 = init_uniform(S.shape[0], k, init_scale_matched(m, k), seed)
         else:
             H0 = H
-        out = fit_full(S, H0, default_lr(m, k), iters, tol=0.0)
+        if warm_start and H is None and first_max_iters is not None:
+            out = fit_full(S, H0, default_lr(m, k), first_max_iters, tol=first_tol)
+        else:
+            out = fit_full(S, H0, default_lr(m, k), iters, tol=0.0)
         H = out["H"]
         Hs.append(H)
         labs.append(labels(H))

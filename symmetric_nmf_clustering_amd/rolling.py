@@ -71,18 +71,27 @@ def three_sigma(values: np.ndarray, calm: np.ndarray):
     return limit, mean, sd, flags
 
 
+def boundary_share(H: np.ndarray, ratio: float = 0.5) -> float:
+    """Share of rows whose second-largest loading is at least ``ratio`` times
+    their largest (an all-zero row does not count)."""
+    top2 = np.sort(np.asarray(H), axis=1)[:, -2:]
+    return float(np.mean((top2[:, 1] > 0) & (top2[:, 0] >= ratio * top2[:, 1])))
+
+
 def run(stream, *, T: int, windows: int, k: int, iters: int = 100, delta: int = 50,
         kinds=KINDS, warm_start: bool = True, seed: int = 0, tail_frac: float = 0.05,
         monitor_groups=None, keep_H: bool = False, first_max_iters: int = 2000,
         first_tol: float = 1e-6, kmeans: bool = False, kmeans_iters: int = 100,
-        boundary_ratio: float = 0.5) -> dict:
+        boundary_ratio: float = 0.5, S_windows=None) -> dict:
     """Run the rolling workload on ``cuda:0``; returns a dict of per-kind results.
 
     ``stream`` is a ``synth.Stream`` (host); its returns are copied to the device
     once and every window is a view of that copy. With ``kmeans`` every window
     also gets the spherical k-means baseline on the same S (seeded the same in
     every window), its agreement with the SymNMF labels, and the share of
-    boundary instruments in H."""
+    boundary instruments in H. ``S_windows`` (optional, one n x n host array per
+    kind and window: ``S_windows[kind][t]``) supplies the dependence matrices
+    instead of building them from the returns (a caller's own estimator)."""
     import torch
 
     from . import api, metrics
@@ -120,7 +129,10 @@ def run(stream, *, T: int, windows: int, k: int, iters: int = 100, delta: int = 
         torch.cuda.synchronize()
         for t in range(windows):
             c0 = time.perf_counter()
-            api.build_S(Xd[t:t + T], kind, tail_frac, out=S)
+            if S_windows is None:
+                api.build_S(Xd[t:t + T], kind, tail_frac, out=S)
+            else:
+                S.copy_(torch.from_numpy(np.ascontiguousarray(S_windows[kind][t], dtype=np.float32)))
             torch.cuda.synchronize()
             c1 = time.perf_counter()
             if warm_start and H is not None:
@@ -145,8 +157,7 @@ def run(stream, *, T: int, windows: int, k: int, iters: int = 100, delta: int = 
             d_host = dg.cpu().numpy()
             Hh = H.cpu().numpy()
             c3 = time.perf_counter()
-            top2 = np.sort(Hh, axis=1)[:, -2:]
-            boundary[t] = float(np.mean((top2[:, 1] > 0) & (top2[:, 0] >= boundary_ratio * top2[:, 1])))
+            boundary[t] = boundary_share(Hh, boundary_ratio)
             if kmeans:
                 km = api.spherical_kmeans(S, k, max_iters=kmeans_iters, seed=seed)
                 km_lab = km.labels.cpu().numpy()

@@ -1,18 +1,19 @@
 """The rolling workload on the GPU.
 
-Small stream (n = 768, 41 windows of 160 days): every window against the oracle
-from the same S and init — objective at the first and last step, labels, the
-stressed-sector block means of S — and the ARI series and 3-sigma limit built
-on them. Full stream (n = 20 000, 250 windows of 252 days, the rolling
+Small stream (n = 768, 41 windows of 160 days), on the oracle's S of every
+window: the |corr| chain end to end and the TPDM chain link by link against the
+oracle — objectives, labels, the stressed-sector block means, the k-means
+baseline, the ARI series and its 3-sigma limit. Full stream (n = 20 000, 250 windows of 252 days, the rolling
 workload): properties that hold at any size (labels valid, every fit descends,
 the alert fires only once the switch fills a large share of the window, the
 co-crash raises the TPDM's cross-sector dependence)."""
 import numpy as np
 import pytest
+from sklearn.metrics import adjusted_rand_score
 
 import oracle
 from symmetric_nmf_clustering_amd import synth
-from tests.gpu_util import require_gpu, s_close
+from tests.gpu_util import S_to_dev, require_gpu, to_dev
 
 pytestmark = pytest.mark.gpu
 
@@ -23,78 +24,114 @@ SMALL = dict(n=768, k=6, days=200, switch_day=150, switch_frac=0.05, stress_grou
 T_SMALL, W_SMALL, DELTA_SMALL, ITERS = 160, 41, 10, 100
 
 
+def _oracle_S(st, kind):
+    """Each window's S built by the oracle from the returns, rounded to fp32:
+    the input both sides factorize."""
+    out = []
+    for t in range(W_SMALL):
+        Xw = st.window(t, T_SMALL)
+        S = oracle.abs_corr(Xw) if kind == "abscorr" else oracle.tpdm(Xw)
+        out.append(S.astype(np.float32))
+    return out
+
+
 @pytest.fixture(scope="module")
 def small():
     require_gpu()
     from symmetric_nmf_clustering_amd import rolling
     st = synth.rolling_stream(**SMALL)
+    S_win = {kind: _oracle_S(st, kind) for kind in ("abscorr", "tpdm")}
     res = rolling.run(st, T=T_SMALL, windows=W_SMALL, k=SMALL["k"], iters=ITERS,
-                      delta=DELTA_SMALL, keep_H=True, kmeans=True)
-    return st, res
+                      delta=DELTA_SMALL, keep_H=True, kmeans=True, S_windows=S_win)
+    return st, S_win, res
 
 
-@pytest.mark.parametrize("kind", ["abscorr", "tpdm"])
-def test_rolling_small_matches_oracle(small, kind):
-    """Every window against the oracle from the same input: the device-built
-    fp32 S of the window and the same init (the seeded init for the first
-    window, fitted to convergence; the device's previous-window H after it,
-    100 full-batch steps).
-    Parity is defined per link of the warm-started chain: run end to end, two
-    chains that differ in rounding drift apart over thousands of steps. The
-    builds are checked against the oracle's own S on the first and last
-    window."""
-    torch = require_gpu()
-    from symmetric_nmf_clustering_amd import api
-    st, res = small
-    r = res["kinds"][kind]
-    n, k = SMALL["n"], SMALL["k"]
-    groups = st.stress_groups
-    ref_labels = []
+def test_rolling_small_corr_chain_matches_oracle(small):
+    """|corr|: the whole warm-started chain (first window to convergence, then
+    100 steps per window) on the oracle's S of every window, against the
+    oracle's chain from the same seeded init: objective at the first and last
+    step of every window, labels, the stressed sectors' block means, the
+    k-means baseline's agreement with SymNMF, the boundary share, and the ARI
+    series with its 3-sigma limit. (On |corr| two chains that differ only in
+    rounding stay together; see the TPDM test for the per-window form.)"""
+    st, S_win, res = small
+    r = res["kinds"]["abscorr"]
+    k = SMALL["k"]
+    ref = oracle.rolling_fit(st.X, k, T_SMALL, W_SMALL, kind="abscorr", iters=ITERS,
+                             S_windows=S_win["abscorr"], first_max_iters=2000, first_tol=1e-6)
     for t in range(W_SMALL):
-        Xw = st.window(t, T_SMALL)
-        S = api.build_S(torch.from_numpy(np.ascontiguousarray(Xw)).cuda(), kind)[0]
-        S = S.cpu().numpy().astype(np.float64)
-        assert S.shape == (n, n)
-        if t in (0, W_SMALL - 1):
-            S_own = oracle.abs_corr(Xw) if kind == "abscorr" else oracle.tpdm(Xw)
-            ok, worst = s_close(S.astype(np.float32), S_own)
-            assert ok, (t, worst)
-        m = S.mean()
-        if t == 0:
-            # the first window is fitted to convergence; where fp32 noise in f
-            # decides the exact stop step, parity means the same number of
-            # steps: the oracle takes the device's count (f_t of the stop step
-            # t needs one step more)
-            H0 = oracle.init_uniform(n, k, oracle.init_scale_matched(m, k), 0)
-            steps = r["first_window_iters"] + (1 if r["first_window_converged"] else 0)
-            assert r["first_window_iters"] > ITERS
-            ref = oracle.fit_full(S, H0, oracle.default_lr(m, k), steps, tol=0.0)
-        else:
-            H0 = r["H"][t - 1].astype(np.float64)
-            ref = oracle.fit_full(S, H0, oracle.default_lr(m, k), ITERS)
+        S = S_win["abscorr"][t].astype(np.float64)
         s2 = float((S * S).sum())
-        for got, want in ((r["f_first"][t], ref["f"][0]), (r["f_last"][t], ref["f"][-1])):
+        fr = ref["f"][t]
+        for got, want in ((r["f_first"][t], fr[0]), (r["f_last"][t], fr[-1])):
             assert abs(got - want) <= 1e-3 * max(abs(want), 1e-6 * s2), (t, got, want)
-        lab = oracle.labels(ref["H"])
-        a = oracle.ari(r["labels"][t], lab)
-        assert a >= 0.99, (t, a)
-        ref_labels.append(lab)
-        B = oracle.cross_block_means(S, st.labels_after, groups)
+        assert adjusted_rand_score(r["labels"][t], ref["labels"][t]) >= 0.99, t
+        B = oracle.cross_block_means(S, st.labels_after, st.stress_groups)
         np.testing.assert_allclose(r["block_means"][t], B, rtol=1e-5)
-        # the boundary share of the device's H, and the k-means baseline on
-        # the same S against the oracle's from the same seeded rows
-        assert r["boundary_fraction"][t] == oracle.boundary_fraction(r["H"][t])
+        assert abs(r["boundary_fraction"][t] - oracle.boundary_fraction(ref["H"][t])) <= 0.01, t
         km = oracle.spherical_kmeans(S, k, seed=0)
-        a_km = oracle.ari(km["labels"], r["labels"][t])
-        assert abs(r["kmeans_vs_symnmf_ari"][t] - a_km) <= 0.02, (t, r["kmeans_vs_symnmf_ari"][t], a_km)
-    # the ARI series and its limit, from the oracle's labels
-    d_ref = oracle.ari_drift(ref_labels, DELTA_SMALL)
+        want = adjusted_rand_score(km["labels"], ref["labels"][t])
+        assert abs(r["kmeans_vs_symnmf_ari"][t] - want) <= 0.02, (t, r["kmeans_vs_symnmf_ari"][t], want)
+    d_ref = oracle.ari_drift(ref["labels"], DELTA_SMALL)
     np.testing.assert_allclose(r["ari_drift"], d_ref, atol=0.02)
     calm = oracle.calm_windows(W_SMALL, T_SMALL, DELTA_SMALL, SMALL["switch_day"],
                                SMALL["stress_first"], SMALL["stress_last"])
     np.testing.assert_array_equal(res["calm"], calm)
-    lim_ref = oracle.control_limit(d_ref, calm)[0]
-    assert abs(r["limit"] - lim_ref) <= 0.05
+    assert abs(r["limit"] - oracle.control_limit(d_ref, calm)[0]) <= 0.05
+
+
+def test_rolling_small_tpdm_links_match_oracle(small):
+    """TPDM: each link of the warm-started chain from the same input — the
+    oracle's S of window t and the oracle chain's H of window t-1 (the seeded
+    init for window 0) — on the device through the C ABI against the oracle.
+
+    A warm start sits near a stationary point, and AdaGrad's first step moves
+    every coordinate by lr sign(g) (G starts at 0), so where many gradients are
+    at rounding level fp32 and fp64 take different signs and the two
+    trajectories part (several correct results). What is unique is compared:
+    the first step on every coordinate whose gradient is decided
+    (|g| > 1e-3 max|g|), and the whole 100-step objective trajectory (1e-3) on
+    links where fewer than 5% of the coordinates are undecided. On the other
+    links the outcome must be valid and comparable: H >= 0, the objective
+    falls, ends within 5% of the oracle's, labels agree (ARI >= 0.9). The
+    driver's own TPDM chain is checked for its block means."""
+    torch = require_gpu()
+    from symmetric_nmf_clustering_amd import api
+    st, S_win, res = small
+    k = SMALL["k"]
+    H_prev = None
+    strict = 0
+    for t in range(W_SMALL):
+        S = S_win["tpdm"][t].astype(np.float64)
+        m = S.mean()
+        lr = oracle.default_lr(m, k)
+        H0 = (oracle.init_uniform(S.shape[0], k, oracle.init_scale_matched(m, k), 0)
+              if H_prev is None else H_prev.astype(np.float32).astype(np.float64))
+        Sd, H0d = S_to_dev(S_win["tpdm"][t], torch), to_dev(H0, torch)
+        # the first step on decided coordinates
+        ref1 = oracle.fit_full(S, H0, lr, 1)
+        one = api.fit(Sd, k, solver="full", max_iters=1, tol_rel=0.0, H0=H0d).H.cpu().numpy()
+        g = oracle.gradient(S, H0)
+        decided = np.abs(g) > 1e-3 * np.abs(g).max()
+        assert np.abs(one - ref1["H"])[decided].max() <= 1e-4 * lr, t
+        assert one.min() >= 0.0 and np.abs(one - H0).max() <= lr * (1 + 1e-5), t
+        # 100 steps
+        ref = oracle.fit_full(S, H0, lr, ITERS)
+        got = api.fit(Sd, k, solver="full", max_iters=ITERS, tol_rel=0.0, H0=H0d)
+        s2 = float((S * S).sum())
+        fg, fr = got.f_trace, np.asarray(ref["f"])
+        Hg = got.H.cpu().numpy()
+        assert Hg.min() >= 0.0 and fg[-1] < fg[0], t
+        if np.mean(~decided) < 0.05:
+            strict += 1
+            assert np.all(np.abs(fg - fr) <= 1e-3 * np.maximum(np.abs(fr), 1e-6 * s2)), t
+        else:
+            assert abs(fg[-1] - fr[-1]) <= 0.05 * fr[-1], (t, fg[-1], fr[-1])
+            assert adjusted_rand_score(Hg.argmax(axis=1), oracle.labels(ref["H"])) >= 0.9, t
+        H_prev = ref["H"]
+        B = oracle.cross_block_means(S, st.labels_after, st.stress_groups)
+        np.testing.assert_allclose(res["kinds"]["tpdm"]["block_means"][t], B, rtol=1e-5)
+    assert strict >= 10
 
 
 def test_rolling_small_cold_start_is_per_window_seeded_fit():

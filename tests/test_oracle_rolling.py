@@ -182,3 +182,12 @@ def test_boundary_fraction_hand_case():
     # ratios of second to first loading: 0, 0.6, 0.4, (zero row), 0.49, 0.5
     H = np.array([[1.0, 0.0], [1.0, 0.6], [0.4, 1.0], [0.0, 0.0], [1.0, 0.49], [0.5, 1.0]])
     assert oracle.boundary_fraction(H) == pytest.approx(2 / 6)
+
+
+def test_library_boundary_share_matches_oracle():
+    rng = np.random.default_rng(8)
+    H = rng.random((500, 6)) ** 4
+    H[::7] = 0.0
+    H[3] = [1.0, 0.5, 0, 0, 0, 0]  # exactly at the ratio
+    for ratio in (0.3, 0.5, 0.9):
+        assert rolling.boundary_share(H, ratio) == oracle.boundary_fraction(H, ratio)
