@@ -174,7 +174,11 @@ def run(stream, *, T: int, windows: int, k: int, iters: int = 100, delta: int = 
         drift = np.full(windows, np.nan)
         for t in range(delta, windows):
             drift[t] = metrics.adjusted_rand_index(labs[t - delta], labs[t])
-        limit, mean, sd, flags = three_sigma(drift, calm)
+        if calm.sum() >= 2:
+            limit, mean, sd, flags = three_sigma(drift, calm)
+        else:  # too few windows to calibrate (e.g. a run shorter than delta)
+            limit = mean = sd = float("nan")
+            flags = np.zeros(windows, dtype=bool)
         m = len(groups)
         off = ~np.eye(m, dtype=bool)
         pair_w = np.outer(sizes, sizes)[off]
@@ -198,6 +202,11 @@ def run(stream, *, T: int, windows: int, k: int, iters: int = 100, delta: int = 
     return out
 
 
+def _num(x):
+    x = float(x)
+    return x if np.isfinite(x) else None
+
+
 def summary(res: dict, stream) -> dict:
     """A JSON-able digest: timings, the drift dip and its alert, the co-crash."""
     T, W = res["T"], res["windows"]
@@ -215,15 +224,19 @@ def summary(res: dict, stream) -> dict:
             "build_ms_mean": 1e3 * float(r["build_s"].mean()),
             "fit_ms_mean": 1e3 * float(r["fit_s"].mean()),
             "total_s": float(per.sum()),
-            "calm_ari_mean": r["calm_mean"], "calm_ari_sd": r["calm_sd"], "limit": r["limit"],
-            "min_drift": float(np.nanmin(dr)), "min_drift_window": int(np.nanargmin(dr)),
+            "calm_ari_mean": _num(r["calm_mean"]), "calm_ari_sd": _num(r["calm_sd"]),
+            "limit": _num(r["limit"]),
+            "min_drift": _num(np.nanmin(dr)) if np.isfinite(dr).any() else None,
+            "min_drift_window": int(np.nanargmin(dr)) if np.isfinite(dr).any() else None,
             "flagged_windows": int(flagged.size),
             "first_flag": int(flagged[0]) if flagged.size else None,
             "first_window_iters": int(r["first_window_iters"]),
-            "cross_dependence_calm": float(r["cross_dependence"][~holds_stress].mean()),
+            "cross_dependence_calm": _num(r["cross_dependence"][~holds_stress].mean())
+            if (~holds_stress).any() else None,
             "cross_dependence_stress_peak": float(r["cross_dependence"][holds_stress].max())
             if holds_stress.any() else None,
-            "cross_dependence_scaled_calm": float(r["cross_dependence_scaled"][~holds_stress].mean()),
+            "cross_dependence_scaled_calm": _num(r["cross_dependence_scaled"][~holds_stress].mean())
+            if (~holds_stress).any() else None,
             "cross_dependence_scaled_stress_peak":
                 float(r["cross_dependence_scaled"][holds_stress].max()) if holds_stress.any() else None,
             "ari_vs_planted_first_window": float(r["ari_vs_before"][0]),

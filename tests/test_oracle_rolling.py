@@ -191,3 +191,22 @@ def test_library_boundary_share_matches_oracle():
     H[3] = [1.0, 0.5, 0, 0, 0, 0]  # exactly at the ratio
     for ratio in (0.3, 0.5, 0.9):
         assert rolling.boundary_share(H, ratio) == oracle.boundary_fraction(H, ratio)
+
+
+def test_library_summary_of_a_run_too_short_to_calibrate():
+    """Fewer windows than delta: no ARI(t - delta, t), no limit; the digest
+    still serialises (None where nothing is defined)."""
+    import json
+    st = _small_stream()
+    W = 5
+    ones = np.ones(W)
+    r = {"build_s": ones * 1e-3, "fit_s": ones * 1e-2, "monitor_s": ones * 1e-3,
+         "flags": np.zeros(W, bool), "ari_drift": np.full(W, np.nan), "calm_mean": float("nan"),
+         "calm_sd": float("nan"), "limit": float("nan"), "first_window_iters": 10,
+         "cross_dependence": ones, "cross_dependence_scaled": ones, "ari_vs_before": ones,
+         "ari_vs_after": ones, "boundary_fraction": ones * 0}
+    res = {"T": 30, "windows": W, "n": 480, "k": 6, "iters": 10, "delta": 50, "warm_start": True,
+           "calm": np.zeros(W, bool), "kinds": {"abscorr": r}}
+    d = json.loads(json.dumps(rolling.summary(res, st), allow_nan=False))
+    k = d["kinds"]["abscorr"]
+    assert k["limit"] is None and k["min_drift"] is None and k["first_flag"] is None
