@@ -15,23 +15,41 @@
 
 namespace symnmf {
 
-// ---- S statistics: per 64-row block, sum S and sum S^2 (accumulated in fp64) ---
+// ---- S statistics: per kStatsRows-row block, sum S and sum S^2 (fp64) ---------
+// 16-byte loads (lds is a multiple of 4 and S 16-byte aligned) and eight
+// independent fp64 accumulators per thread, so the pass is bound by HBM rather
+// than by the latency of one fp64 addition chain. The summation order depends
+// only on n, so the result is reproducible.
 __global__ __launch_bounds__(256) void s_stats_kernel(const float* __restrict__ S, int64_t lds,
                                                       int n, double* __restrict__ part2) {
     __shared__ double red[4];
-    const int row0 = blockIdx.x * 64;
-    const int rows = min(64, n - row0);
-    double s1 = 0.0, s2 = 0.0;
+    const int row0 = blockIdx.x * kStatsRows;
+    const int rows = min(kStatsRows, n - row0);
+    const int n4 = n >> 2;
+    double a0 = 0.0, a1 = 0.0, a2 = 0.0, a3 = 0.0;
+    double b0 = 0.0, b1 = 0.0, b2 = 0.0, b3 = 0.0;
     for (int rr = 0; rr < rows; ++rr) {
         const float* row = S + (int64_t)(row0 + rr) * lds;
-        for (int c = threadIdx.x; c < n; c += 256) {
-            const double v = (double)row[c];
-            s1 += v;
-            s2 += v * v;
+        for (int q = threadIdx.x; q < n4; q += 256) {
+            const float4 v = *reinterpret_cast<const float4*>(row + 4 * q);
+            const double x = v.x, y = v.y, z = v.z, w = v.w;
+            a0 += x;
+            a1 += y;
+            a2 += z;
+            a3 += w;
+            b0 = fma(x, x, b0);
+            b1 = fma(y, y, b1);
+            b2 = fma(z, z, b2);
+            b3 = fma(w, w, b3);
+        }
+        for (int c = 4 * n4 + (int)threadIdx.x; c < n; c += 256) {
+            const double x = row[c];
+            a0 += x;
+            b0 = fma(x, x, b0);
         }
     }
-    const double t1 = block_sum256(s1, red);
-    const double t2 = block_sum256(s2, red);
+    const double t1 = block_sum256((a0 + a1) + (a2 + a3), red);
+    const double t2 = block_sum256((b0 + b1) + (b2 + b3), red);
     if (threadIdx.x == 0) {
         part2[2 * blockIdx.x] = t1;
         part2[2 * blockIdx.x + 1] = t2;
@@ -55,7 +73,7 @@ __global__ __launch_bounds__(256) void s_stats_final_kernel(const double* __rest
 }
 
 hipError_t launch_s_stats(const float* S, int64_t lds, int n, double* part2, hipStream_t st) {
-    const int nblk = (n + 63) / 64;
+    const int nblk = (n + kStatsRows - 1) / kStatsRows;
     hipLaunchKernelGGL(s_stats_kernel, dim3(nblk), dim3(256), 0, st, S, lds, n, part2);
     return hipGetLastError();
 }

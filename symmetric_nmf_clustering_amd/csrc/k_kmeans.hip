@@ -113,19 +113,20 @@ hipError_t launch_onehot_scaled(const int32_t* lab, const float* rinv, int n, in
 }
 
 // Column sums of squares of C (n x k), fp64 partials per block of 256 rows:
-// part[b * k + j]. Thread j < k of block b walks the block's rows in order.
-__global__ __launch_bounds__(64) void col_sumsq_kernel(const float* __restrict__ C, int n, int k,
-                                                       double* __restrict__ part) {
-    const int j = threadIdx.x;
-    if (j >= k) return;
-    const int64_t r0 = (int64_t)blockIdx.x * 256;
-    const int64_t r1 = min((int64_t)n, r0 + 256);
-    double s = 0.0;
-    for (int64_t r = r0; r < r1; ++r) {
-        const double v = C[r * k + j];
-        s += v * v;
+// part[b * k + j]. Block (b, j) reduces column j over its 256 rows in a fixed
+// order.
+__global__ __launch_bounds__(256) void col_sumsq_kernel(const float* __restrict__ C, int n, int k,
+                                                        double* __restrict__ part) {
+    __shared__ double red[4];
+    const int j = blockIdx.y;
+    const int64_t r = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    double v = 0.0;
+    if (r < n) {
+        const double c = C[r * k + j];
+        v = c * c;
     }
-    part[(int64_t)blockIdx.x * k + j] = s;
+    v = block_sum256(v, red);
+    if (threadIdx.x == 0) part[(int64_t)blockIdx.x * k + j] = v;
 }
 
 // norm[j] = sqrt(sum_b part[b * k + j]), blocks folded in order.
@@ -153,7 +154,8 @@ __global__ __launch_bounds__(256) void col_scale_kernel(const float* __restrict_
 hipError_t launch_normalize_columns(const float* C, int n, int k, double* part, double* norm,
                                     float* Ct, hipStream_t st) {
     const int nblk = (n + 255) / 256;
-    hipLaunchKernelGGL(col_sumsq_kernel, dim3((unsigned)nblk), dim3(64), 0, st, C, n, k, part);
+    hipLaunchKernelGGL(col_sumsq_kernel, dim3((unsigned)nblk, (unsigned)k), dim3(256), 0, st, C, n,
+                       k, part);
     hipLaunchKernelGGL(col_fold_kernel, dim3(1), dim3(64), 0, st, part, nblk, k, norm);
     const int64_t count = (int64_t)n * k;
     hipLaunchKernelGGL(col_scale_kernel, dim3((unsigned)((count + 255) / 256)), dim3(256), 0, st,

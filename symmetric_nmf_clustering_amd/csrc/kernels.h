@@ -69,6 +69,9 @@ hipError_t launch_reduce_partials(const float* part, int nsplit, int n, int widt
                                   float* P, const float* Hdot, double* tr_part, hipStream_t st);
 
 // ---- fit --------------------------------------------------------------------
+constexpr int kStatsRows = 16;  // rows of S per block of the statistics pass
+// part2[2b], part2[2b+1] = sum and sum of squares of S over rows
+// [kStatsRows b, kStatsRows (b+1)) (fp64); ceil(n / kStatsRows) blocks.
 hipError_t launch_s_stats(const float* S, int64_t lds, int n, double* part2, hipStream_t st);
 hipError_t launch_s_stats_final(const double* part2, int nblk, double* out2, hipStream_t st);
 hipError_t launch_init_uniform(float* H, int64_t count, double scale, double shift, uint64_t seed,

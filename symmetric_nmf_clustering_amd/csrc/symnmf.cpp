@@ -316,7 +316,7 @@ size_t fit_layout(void* ws, int64_t n, int k, int max_iters, int block_rows, Fit
     l.part = c.take<float>((size_t)kMaxSplits * n * ldp_of(k));
     l.gram_part = c.take<float>((size_t)nblk * k * k);
     l.tr_part = c.take<double>((size_t)nblk);
-    l.stats_part = c.take<double>((size_t)2 * cdiv(n, 64));
+    l.stats_part = c.take<double>((size_t)2 * cdiv(n, kStatsRows));
     l.stats_out = c.take<double>(2);
     l.blocks = c.take<int>((size_t)2 * nb + 16);
     l.zero_rows = c.take<int>(1);
@@ -725,7 +725,7 @@ int symnmf_fit(const float* S, int64_t n, int64_t lds, int32_t k, const symnmf_f
 
     // ---- ||S||^2 and mean(S) (one pass over S)
     HIPCHK(launch_s_stats(S, lds, nn, L.stats_part, st));
-    HIPCHK(launch_s_stats_final(L.stats_part, (int)cdiv(n, 64), L.stats_out, st));
+    HIPCHK(launch_s_stats_final(L.stats_part, (int)cdiv(n, kStatsRows), L.stats_out, st));
     double stats[2];
     HIPCHK(hipMemcpyAsync(stats, L.stats_out, sizeof(stats), hipMemcpyDeviceToHost, st));
     HIPCHK(hipStreamSynchronize(st));
