@@ -65,11 +65,14 @@ __device__ __forceinline__ bool split_segment(const RowPlan& rp, int s, int g, i
 // MFMA tile beside the vector-ALU columns, i.e. k <= 24, or MFMA tiles only)
 // are bound by HBM: the more rows of S one wave has in flight the better, and
 // six groups (24 rows, 12 KiB per wave) still leave two waves per SIMD. The
-// wide shapes are bound by the matrix core, and the multi-segment variant
-// carries an extra loop level; both keep two groups (deeper trips only cost
-// occupancy there).
+// wide shapes (CW = 1, three or more MFMA tiles) are bound by the matrix
+// core, where more waves per SIMD beat deeper trips: one group per trip keeps
+// the 80-column probe pass at four waves per SIMD (15.7 ms at n = 100 000
+// against 17.3 ms with two groups and three waves). The multi-segment variant
+// carries an extra loop level and keeps two groups.
 constexpr int sh_rows_per_trip(int ncm, int nv, int cw, int rm) {
-    return (cw == 2 && rm != kRowsBlocksMulti && (ncm <= 1 || nv == 0)) ? 6 : 2;
+    if (cw < 2) return 1;
+    return (rm != kRowsBlocksMulti && (ncm <= 1 || nv == 0)) ? 6 : 2;
 }
 
 // NCM MFMA column tiles (16 columns each) plus NV <= 8 columns on the vector
