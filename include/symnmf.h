@@ -99,6 +99,10 @@ typedef struct symnmf_fit_params {
     int32_t check_every;   /* host polls the device stop flag every this many steps;
                               results do not depend on it; default 16                   */
     int32_t resume;        /* 1: G holds the AdaGrad accumulator on entry (needs G)     */
+    double rms_decay;      /* 0 (default): AdaGrad, G += g*g. In (0, 1): RMSprop, one of
+                              the AdaGrad-family solvers of P3's abstract (Tieleman and
+                              Hinton 2012): G = rms_decay G + (1 - rms_decay) g*g; the
+                              projected step is unchanged. Applies to every step.      */
 } symnmf_fit_params;
 
 typedef struct symnmf_fit_report {

@@ -38,7 +38,7 @@ __all__ = [
     "standardize", "abs_corr", "abs_corr_rows", "tpdm_angles", "tpdm",
     "tpdm_rows", "splitmix64", "uniform24", "init_uniform", "init_scale_matched",
     "default_lr", "sh_product", "objective_explicit", "objective_trace", "gradient",
-    "adagrad_step", "fit_full", "sample_blocks", "svrg_sh_estimate",
+    "adagrad_step", "rmsprop_step", "fit_full", "sample_blocks", "svrg_sh_estimate",
     "gap_ratio", "initial_blocks", "fit_adaptgrow", "top_eigenvalues",
     "ari_drift", "calm_windows", "control_limit", "cross_block_means", "rolling_fit",
     "spherical_kmeans", "boundary_fraction",
@@ -219,13 +219,27 @@ def adagrad_step(H, G, g, lr, eps=1e-8):
     return H, G
 
 
+def rmsprop_step(H, G, g, lr, rho, eps=1e-8):
+    """RMSprop (Tieleman and Hinton 2012), one of the AdaGrad-family solvers the
+    P3 abstract names: the squared-gradient accumulator becomes an exponential
+    moving average, G <- rho G + (1 - rho) g*g, with the same projected step
+    H <- max(H - lr g / (sqrt(G) + eps), 0) as AdaGrad."""
+    G = rho * G + (1.0 - rho) * (g * g)
+    H = np.maximum(H - lr * g / (np.sqrt(G) + eps), 0.0)
+    return H, G
+
+
+def _step(H, G, g, lr, eps, rho):
+    return adagrad_step(H, G, g, lr, eps) if not rho else rmsprop_step(H, G, g, lr, rho, eps)
+
+
 # --------------------------------------------------------------------------
 # Full-batch projected AdaGrad (P1 "Factorizing with SymNMF"; P2 sketch).
 # --------------------------------------------------------------------------
 
 
-def fit_full(S, H0, lr, max_iters, tol=0.0, eps=1e-8, G0=None, objective="trace"):
-    """Full-batch projected AdaGrad.
+def fit_full(S, H0, lr, max_iters, tol=0.0, eps=1e-8, G0=None, objective="trace", rho=0.0):
+    """Full-batch projected AdaGrad (RMSprop's accumulator when rho > 0).
 
     Iteration t: P = S H_t; f_t = f(H_t) (before the update); if t >= 1 and
     |f_{t-1} - f_t| < tol * |f_{t-1}|, stop and return H_t; otherwise take the
@@ -247,7 +261,7 @@ def fit_full(S, H0, lr, max_iters, tol=0.0, eps=1e-8, G0=None, objective="trace"
             converged = True
             break
         g = 4.0 * (H @ (H.T @ H) - P)
-        H, G = adagrad_step(H, G, g, lr, eps)
+        H, G = _step(H, G, g, lr, eps, rho)
         t += 1
     return dict(H=H, G=G, f=fs, iters=t, converged=converged)
 
@@ -310,7 +324,7 @@ def initial_blocks(gamma, nb, threshold=5.0):
 
 def fit_adaptgrow(S, H0, lr, max_iters, *, solver=SOLVER_AUTO, eigvals=None, k=None,
                   phi0=0.0, block_rows=1024, gap_threshold=5.0, tol=1e-6,
-                  stall_tol=1e-3, eps=1e-8, seed=0):
+                  stall_tol=1e-3, eps=1e-8, seed=0, rho=0.0):
     """AdaptGrow: full-batch AdaGrad or Block-SVRG with sample growth.
 
     Branch choice: FULL -> full; otherwise |B|0 from phi0 > 0
@@ -388,7 +402,7 @@ def fit_adaptgrow(S, H0, lr, max_iters, *, solver=SOLVER_AUTO, eigvals=None, k=N
             if epoch_pos >= E:
                 epoch_pos = 0
         g = 4.0 * (H @ K - P)
-        H, G = adagrad_step(H, G, g, lr, eps)
+        H, G = _step(H, G, g, lr, eps, rho)
         t += 1
     return dict(H=H, G=G, f=fs, iters=t, converged=converged, history=history,
                 gamma=gamma, start_branch=start_branch,

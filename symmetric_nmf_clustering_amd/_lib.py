@@ -48,6 +48,7 @@ class FitParams(ctypes.Structure):
         ("seed", ctypes.c_uint64),
         ("check_every", ctypes.c_int32),
         ("resume", ctypes.c_int32),
+        ("rms_decay", ctypes.c_double),
     ]
 
 

@@ -124,7 +124,7 @@ hipError_t launch_copy(float* dst, const float* src, int64_t count, hipStream_t 
 //   P   = sum_s part[s][i][c]            (exact pass, fixed split order)
 //      or P~[i][c] + pscale * sum_s ...  (Block-SVRG estimate)
 //   g   = 4 ((H K)[i][c] - P)
-//   G'  = G + g*g
+//   G'  = G + g*g   (RMSprop: decay G + (1 - decay) g*g)
 //   H'  = max(H - lr g / (sqrt(G') + eps), 0)
 // plus <H_t, P> per block (fp64) for the trace identity and the partial Gram
 // H'^T H' of the block's rows for the next step's K.
@@ -172,7 +172,9 @@ __global__ __launch_bounds__(256) void update_kernel(UpdateArgs a) {
             for (int d = 0; d < k; ++d) hk = fmaf(hrow[d], Ks[d * k + c], hk);
             const float h = hrow[c];
             const float g = 4.f * (hk - P);
-            const float Gv = a.G[gi * k + c] + g * g;
+            const float Gold = a.G[gi * k + c];
+            const float Gv = a.decay > 0.f ? a.decay * Gold + (1.f - a.decay) * (g * g)
+                                           : Gold + g * g;
             const float hn = fmaxf(h - a.lr * g / (sqrtf(Gv) + a.eps), 0.f);
             a.Gn[gi * k + c] = Gv;
             a.Hn[gi * k + c] = hn;

@@ -94,6 +94,7 @@ struct UpdateArgs {
     float* Pa;           // anchor P~ <- P_t (nullable)
     FitDev* fd;
     float lr, eps;
+    float decay;         // 0: AdaGrad accumulator; in (0, 1): RMSprop moving average
     double* tr_part;     // per block <H_t, P_t> (nullable)
     float* gram_part;    // per block partial Gram of the rows written (k x k)
     int gram_only;       // 1: no update, Gram partials of H

@@ -391,6 +391,7 @@ void symnmf_fit_params_default(symnmf_fit_params* p) {
     p->seed = 0;
     p->check_every = 16;
     p->resume = 0;
+    p->rms_decay = 0.0;
 }
 
 size_t symnmf_workspace_bytes(int op, int64_t n, int32_t k_or_p, int64_t T,
@@ -705,6 +706,7 @@ int symnmf_fit(const float* S, int64_t n, int64_t lds, int32_t k, const symnmf_f
         lds % 4 || !aligned(S, 16) || !aligned(H, 4))
         return SYMNMF_E_INVALID;
     if (P.solver < 0 || P.solver > 2 || P.max_iters < 0 || !(P.eps > 0.0) || P.block_rows < 4 ||
+        !(P.rms_decay >= 0.0 && P.rms_decay < 1.0) ||
         !(P.tol_rel >= 0.0) || !(P.stall_tol >= 0.0) || P.init < 0 || P.init > 2 ||
         !(P.gap_threshold > 0.0) || (P.resume && !G) || (obj_trace_cap > 0 && !obj_trace_host) ||
         obj_trace_cap < 0 || !std::isfinite(P.lr) || !std::isfinite(P.phi0))
@@ -796,7 +798,7 @@ int symnmf_fit(const float* S, int64_t n, int64_t lds, int32_t k, const symnmf_f
         a.pstride = (int64_t)n * ldp; a.H = L.Hb[cur]; a.G = L.Gb[cur];
         a.Hn = L.Hb[cur ^ 1]; a.Gn = L.Gb[cur ^ 1];
         a.Ha = write_anchor ? L.Ha : nullptr; a.Pa = write_anchor ? L.Pa : nullptr;
-        a.fd = L.fd; a.lr = (float)lr; a.eps = (float)P.eps;
+        a.fd = L.fd; a.lr = (float)lr; a.eps = (float)P.eps; a.decay = (float)P.rms_decay;
         a.tr_part = L.tr_part; a.gram_part = L.gram_part;
         {
             ProfScope ps(SYMNMF_PROF_UPDATE, (double)nk * 4.0 * (5 + fpl.nsplit), st);
@@ -820,7 +822,8 @@ int symnmf_fit(const float* S, int64_t n, int64_t lds, int32_t k, const symnmf_f
         a.n = nn; a.k = k; a.ldp = ldp; a.part = L.part; a.nsplit = sp.nsplit;
         a.pstride = (int64_t)n * ldp; a.Pt = L.Pa; a.pscale = (float)((double)nb / nsel);
         a.H = L.Hb[cur]; a.G = L.Gb[cur]; a.Hn = L.Hb[cur ^ 1]; a.Gn = L.Gb[cur ^ 1];
-        a.fd = L.fd; a.lr = (float)lr; a.eps = (float)P.eps; a.gram_part = L.gram_part;
+        a.fd = L.fd; a.lr = (float)lr; a.eps = (float)P.eps; a.decay = (float)P.rms_decay;
+        a.gram_part = L.gram_part;
         {
             ProfScope ps(SYMNMF_PROF_UPDATE, (double)nk * 4.0 * (6 + sp.nsplit), st);
             HIPCHK(launch_update(a, st));

@@ -177,3 +177,15 @@ def test_fit_argument_validation():
     assert call(P(**full), ws=None) == L.E_WORKSPACE
     assert call(P(**full), wsb=ctypes.c_size_t(1024)) == L.E_WORKSPACE
     assert call(P(**full), ws=ctypes.c_void_p(0x10010)) == L.E_WORKSPACE  # misaligned
+
+
+def test_rms_decay_validated():
+    lib = L.load()
+    z = ctypes.c_size_t(1 << 30)
+    for bad in (-0.1, 1.0, float("nan")):
+        p = L.FitParams()
+        lib.symnmf_fit_params_default(ctypes.byref(p))
+        p.rms_decay = bad
+        rep = L.FitReport()
+        assert lib.symnmf_fit(FAKE, 100, 100, 4, ctypes.byref(p), None, 0, FAKE, None, None, 0,
+                              ctypes.byref(rep), FAKE, z, None) == L.E_INVALID

@@ -136,3 +136,29 @@ def test_sh_product_rows_match_full():
     np.testing.assert_allclose(Pr, P[rows], rtol=1e-14)
     assert trr == pytest.approx(float((H[rows] * P[rows]).sum()), rel=1e-13)
     assert tr == pytest.approx(float(np.trace(H.T @ S @ H)), rel=1e-13)
+
+
+def test_rmsprop_first_step_and_constant_gradient():
+    """RMSprop (Tieleman and Hinton 2012): from G = 0 the first step is
+    lr g / (sqrt(1 - rho) |g| + eps); under a constant gradient the moving
+    average is the geometric sum G_t = (1 - rho^t) g^2; rho = 0 in fit_full is
+    AdaGrad."""
+    rho, lr, eps = 0.9, 0.05, 1e-8
+    H0 = np.array([[1.0, 0.5, 0.2]])
+    g = np.array([[2.0, -0.3, 1e-3]])
+    H1, G1 = oracle.rmsprop_step(H0, np.zeros_like(H0), g, lr, rho, eps)
+    np.testing.assert_allclose(G1, (1 - rho) * g * g, rtol=1e-15)
+    np.testing.assert_allclose(H1, np.maximum(H0 - lr * g / (np.sqrt(1 - rho) * np.abs(g) + eps), 0),
+                               rtol=1e-15)
+    G = np.zeros_like(H0)
+    H = np.full_like(H0, 10.0)
+    for t in range(1, 30):
+        H, G = oracle.rmsprop_step(H, G, g, lr, rho, eps)
+        np.testing.assert_allclose(G, (1 - rho ** t) * g * g, rtol=1e-12)
+    S = _rand_sym(12, 21)
+    Hs = oracle.init_uniform(12, 3, 0.3, 2)
+    a = oracle.fit_full(S, Hs, 0.02, 20, rho=0.0)
+    b = oracle.fit_full(S, Hs, 0.02, 20)
+    np.testing.assert_array_equal(a["H"], b["H"])
+    c = oracle.fit_full(S, Hs, 0.02, 20, rho=0.9)
+    assert not np.array_equal(c["H"], b["H"]) and c["H"].min() >= 0.0
