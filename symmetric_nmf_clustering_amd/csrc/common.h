@@ -58,4 +58,23 @@ __device__ __forceinline__ double block_sum256(double v, double* red) {
     return s;
 }
 
+// sum_{s < count} p[s * stride] added in index order. Eight loads are issued
+// before their additions, so a long sum waits for count/8 memory round trips
+// instead of count; the order of the additions, and so the result, is the
+// same as the plain loop's.
+__device__ __forceinline__ float ordered_strided_sum(const float* __restrict__ p, int count,
+                                                     int64_t stride) {
+    float s = 0.f;
+    int sp = 0;
+    for (; sp + 8 <= count; sp += 8) {
+        float v[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) v[u] = p[(int64_t)(sp + u) * stride];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) s += v[u];
+    }
+    for (; sp < count; ++sp) s += p[(int64_t)sp * stride];
+    return s;
+}
+
 }  // namespace symnmf

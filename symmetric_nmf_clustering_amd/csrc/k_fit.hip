@@ -163,8 +163,7 @@ __global__ __launch_bounds__(256) void update_kernel(UpdateArgs a) {
             const int c = e % k;
             const int64_t gi = (int64_t)(row0 + i);
             const float* p = a.part + gi * a.ldp + c;
-            float s = 0.f;
-            for (int sp = 0; sp < a.nsplit; ++sp) s += p[sp * a.pstride];
+            const float s = ordered_strided_sum(p, a.nsplit, a.pstride);
             float P = s;
             if (a.Pt) P = a.Pt[gi * k + c] + a.pscale * s;
             float hk = 0.f;
@@ -215,50 +214,58 @@ hipError_t launch_update(const UpdateArgs& a, hipStream_t st) {
 }
 
 // ---- per-step finalisation ----------------------------------------------------
-// Workgroup x < k*k folds Gram entry x (upper triangle) over the update blocks;
-// workgroup k*k folds the trace partials. Each sum is split over 256 threads
-// in a fixed stride and combined by a fixed-order tree, so it is
-// deterministic. The last workgroup to finish (counted with an atomic ticket)
-// forms f_t = ||S||^2 - 2 tr + ||K_t||^2, runs the stop test, publishes
-// K_{t+1} and resets the ticket for the next step.
-__global__ __launch_bounds__(256) void finalize_kernel(FitDev* fd, double* f_trace, int t,
-                                                       int nblk, int k,
-                                                       const double* __restrict__ tr_part,
-                                                       const float* __restrict__ gram_part,
-                                                       int flags) {
+// Two launches in stream order (no atomics or fences between workgroups):
+//  * fold: workgroup w < k(k+1)/2 folds upper-triangle Gram entry w (row-major
+//    over x <= y) over the update blocks; the next workgroup folds the trace
+//    partials. Each sum is split over 256 threads in a fixed stride and
+//    combined by a fixed-order tree, so it is deterministic.
+//  * finish (one workgroup): forms f_t = ||S||^2 - 2 tr + ||K_t||^2, runs the
+//    stop test and publishes K_{t+1}.
+__global__ __launch_bounds__(256) void finalize_fold_kernel(FitDev* fd, int nblk, int k,
+                                                            const double* __restrict__ tr_part,
+                                                            const float* __restrict__ gram_part,
+                                                            int flags) {
     if (fd->done) return;
     __shared__ double red[4];
-    __shared__ int last;
     const int tid = threadIdx.x;
+    const int nup = k * (k + 1) / 2;
     const int wg = blockIdx.x;
-    const int kk = k * k;
-    if (wg < kk) {
-        const int x = wg / k;
-        const int y = wg % k;
-        if ((flags & 4) && x <= y) {
-            double s = 0.0;
-            for (int b = tid; b < nblk; b += 256) s += (double)gram_part[(int64_t)b * kk + wg];
-            s = block_sum256(s, red);
-            if (tid == 0) fd->Kd[wg] = s;
+    if (wg < nup) {
+        if (!(flags & 4)) return;
+        // upper-triangle entry number wg -> (x, y), x <= y
+        int x = 0, rem = wg;
+        while (rem >= k - x) {
+            rem -= k - x;
+            ++x;
         }
+        const int y = x + rem;
+        const int e = x * k + y;
+        const int kk = k * k;
+        double s = 0.0;
+        for (int b = tid; b < nblk; b += 256) s += (double)gram_part[(int64_t)b * kk + e];
+        s = block_sum256(s, red);
+        if (tid == 0) fd->Kd[e] = s;
     } else if (flags & 1) {
         double s = 0.0;
         for (int b = tid; b < nblk; b += 256) s += tr_part[b];
         s = block_sum256(s, red);
         if (tid == 0) fd->tr = s;
     }
-    __threadfence();
-    if (tid == 0) last = (atomicAdd(&fd->ticket, 1u) == gridDim.x - 1);
-    __syncthreads();
-    if (!last) return;
-    __threadfence();
+}
+
+__global__ __launch_bounds__(256) void finalize_finish_kernel(FitDev* fd, double* f_trace, int t,
+                                                              int k, int flags) {
+    if (fd->done) return;
+    __shared__ double red[4];
+    const int tid = threadIdx.x;
+    const int kk = k * k;
     if (flags & 4) {
         double k2 = 0.0;
         for (int idx = tid; idx < kk; idx += 256) {
             const int x = idx / k;
             const int y = idx % k;
             if (x <= y) {
-                const double s = ((volatile double*)fd->Kd)[idx];
+                const double s = fd->Kd[idx];
                 fd->K[x * kMaxK + y] = (float)s;
                 fd->K[y * kMaxK + x] = (float)s;
                 k2 += (x == y ? 1.0 : 2.0) * s * s;
@@ -271,8 +278,7 @@ __global__ __launch_bounds__(256) void finalize_kernel(FitDev* fd, double* f_tra
         if (flags & 8) {
             // initial Gram only: no objective, no trace entry
         } else if (flags & 1) {
-            const double tr = *((volatile double*)&fd->tr);
-            const double f = fd->S_fro2 - 2.0 * tr + fd->K2;
+            const double f = fd->S_fro2 - 2.0 * fd->tr + fd->K2;
             if (f_trace) f_trace[t] = f;
             if (!isfinite(f)) {
                 fd->status = -4;
@@ -291,15 +297,16 @@ __global__ __launch_bounds__(256) void finalize_kernel(FitDev* fd, double* f_tra
             fd->f_prev_valid = 0;
         }
         if (flags & 4) fd->K2 = fd->K2next;
-        fd->ticket = 0u;
     }
 }
 
 hipError_t launch_finalize(FitDev* fd, double* f_trace, int t, int nblk, int k,
                            const double* tr_part, const float* gram_part, int flags,
                            hipStream_t st) {
-    hipLaunchKernelGGL(finalize_kernel, dim3(k * k + 1), dim3(256), 0, st, fd, f_trace, t, nblk,
-                       k, tr_part, gram_part, flags);
+    const int nup = k * (k + 1) / 2;
+    hipLaunchKernelGGL(finalize_fold_kernel, dim3(nup + 1), dim3(256), 0, st, fd, nblk, k, tr_part,
+                       gram_part, flags);
+    hipLaunchKernelGGL(finalize_finish_kernel, dim3(1), dim3(256), 0, st, fd, f_trace, t, k, flags);
     return hipGetLastError();
 }
 

@@ -345,8 +345,7 @@ __global__ __launch_bounds__(256) void reduce_partials_kernel(const float* __res
         const int i = row0 + e / width;
         const int c = e % width;
         const float* p = part + (int64_t)i * ldp + c;
-        float s = 0.f;
-        for (int sp = 0; sp < nsplit; ++sp) s += p[sp * pstride];
+        const float s = ordered_strided_sum(p, nsplit, pstride);
         P[(int64_t)i * width + c] = s;
         if (Hdot) acc += (double)Hdot[(int64_t)i * width + c] * (double)s;
     }

@@ -44,7 +44,6 @@ struct FitDev {
     int done;           // once set, every later kernel of the fit returns at once
     int stop_iter;
     int status;         // 0 running, 1 converged, -4 non-finite objective
-    unsigned int ticket;  // finalisation: workgroups done this step
     double tr;            // finalisation scratch: tr(H_t^T P_t)
     double K2next;        // finalisation scratch: ||H_{t+1}^T H_{t+1}||^2
     double Kd[kMaxK * kMaxK];  // finalisation scratch: Gram entries (fp64)
