@@ -90,10 +90,60 @@ __global__ __launch_bounds__(256) void tpdm_ranks_kernel(const float* __restrict
     }
 }
 
+// The same ranks with C columns of the window staged in LDS (losses, T x C):
+// the T x C (day, column) pairs of a workgroup each count, against the staged
+// column, the days with a smaller loss or an equal loss on an earlier day.
+// Consecutive threads take consecutive columns, so the LDS reads of a wave
+// fall in consecutive banks. A column with a non-finite value is skipped and
+// flagged, as above.
+constexpr int kRankLdsFloats = 16000;  // 62.5 KiB of losses per workgroup (+ 256 B of flags)
+
+__global__ __launch_bounds__(256) void tpdm_ranks_lds_kernel(const float* __restrict__ X, int T,
+                                                             int n, int64_t ldx, int C,
+                                                             int* __restrict__ R,
+                                                             int* __restrict__ hist, int* flags) {
+    extern __shared__ float L[];  // L[s * C + c] = loss of day s, column i0 + c
+    __shared__ int bad[64];
+    const int i0 = blockIdx.x * C;
+    const int cols = min(C, n - i0);
+    const int tid = threadIdx.x;
+    if (tid < C) bad[tid] = 0;
+    __syncthreads();
+    for (int e = tid; e < T * C; e += 256) {
+        const int sday = e / C, c = e - (e / C) * C;
+        float v = 0.f;
+        if (c < cols) {
+            v = -X[(int64_t)sday * ldx + i0 + c];
+            if (!isfinite(v)) bad[c] = 1;
+        }
+        L[e] = v;
+    }
+    __syncthreads();
+    if (tid < cols && bad[tid]) atomicOr(&flags[0], 1);
+    for (int e = tid; e < T * C; e += 256) {
+        const int t = e / C, c = e - (e / C) * C;
+        if (c >= cols || bad[c]) continue;
+        const float lt = L[e];
+        int rank = 1;
+        for (int sday = 0; sday < T; ++sday) {
+            const float ls = L[sday * C + c];
+            rank += (ls < lt) || (ls == lt && sday < t);
+        }
+        R[(int64_t)t * n + i0 + c] = rank;
+        atomicAdd(&hist[t * (T + 1) + rank], 1);
+    }
+}
+
 hipError_t launch_tpdm_ranks(const float* X, int T, int n, int64_t ldx, int* R, int* hist,
                              int* flags, hipStream_t st) {
-    hipLaunchKernelGGL(tpdm_ranks_kernel, dim3((n + 255) / 256), dim3(256), 0, st, X, T, n, ldx, R,
-                       hist, flags);
+    if (T <= kRankLdsFloats) {
+        const int C = min(64, kRankLdsFloats / T);
+        hipLaunchKernelGGL(tpdm_ranks_lds_kernel, dim3((unsigned)((n + C - 1) / C)), dim3(256),
+                           (size_t)T * C * sizeof(float), st, X, T, n, ldx, C, R, hist, flags);
+    } else {
+        hipLaunchKernelGGL(tpdm_ranks_kernel, dim3((n + 255) / 256), dim3(256), 0, st, X, T, n,
+                           ldx, R, hist, flags);
+    }
     return hipGetLastError();
 }
 
