@@ -613,16 +613,25 @@ int symnmf_spectral_probe(const float* S, int64_t n, int64_t lds, int32_t p, int
     int rc = orthonormalize(Y, Q, nn, w, L, st);
     if (rc != SYMNMF_OK) return rc;
 
-    std::vector<double> T((size_t)w * w), ev, prev, theta;
-    int it = 0;
-    bool converged = false;
-    for (it = 1; it <= max_iters; ++it) {
+    // One step: Y = S Q and the Rayleigh quotient Q^T Y into L.C, enqueued.
+    auto stage = [&]() -> int {
         {
             ProfScope ps(SYMNMF_PROF_SH_PROBE, 4.0 * n * (double)n + 8.0 * n * w, st);
             HIPCHK(launch_sh_panel(S, lds, Q, w, fp.rp, fp.nsplit, L.part, ldp, st));
         }
         HIPCHK(launch_reduce_partials(L.part, fp.nsplit, nn, w, ldp, Y, nullptr, nullptr, st));
         HIPCHK(launch_crossgram(Q, Y, nn, w, L.cg_part, nblk, L.C, st));
+        return SYMNMF_OK;
+    };
+    // The host eigen-solve of step `it` (which only decides whether to stop)
+    // runs while the device already computes step it+1 from the next Q; if
+    // step `it` converged, that extra step is discarded. The values and the
+    // step count are those of the plain loop.
+    std::vector<double> T((size_t)w * w), ev, prev, theta;
+    int it = 0;
+    bool converged = false;
+    if ((rc = stage())) return rc;
+    for (it = 1; it <= max_iters; ++it) {
         HIPCHK(hipMemcpyAsync(T.data(), L.C, sizeof(double) * w * w, hipMemcpyDeviceToHost, st));
         HIPCHK(hipStreamSynchronize(st));
         for (int i = 0; i < w; ++i)
@@ -632,6 +641,11 @@ int symnmf_spectral_probe(const float* S, int64_t n, int64_t lds, int32_t p, int
             }
         for (double v : T)
             if (!std::isfinite(v)) return SYMNMF_E_NONFINITE;
+        if (it < max_iters) {
+            rc = orthonormalize(Y, Q, nn, w, L, st);
+            if (rc != SYMNMF_OK) return rc;
+            if ((rc = stage())) return rc;
+        }
         std::vector<double> A = T;
         jacobi_eig(w, A, ev, nullptr);
         std::vector<int> order(w);
@@ -650,9 +664,8 @@ int symnmf_spectral_probe(const float* S, int64_t n, int64_t lds, int32_t p, int
         }
         prev = theta;
         if (it == max_iters) break;
-        rc = orthonormalize(Y, Q, nn, w, L, st);
-        if (rc != SYMNMF_OK) return rc;
     }
+    HIPCHK(hipStreamSynchronize(st));  // a discarded step may still be running
     for (int i = 0; i < p; ++i) eigvals_host[i] = theta[i];
     if (iters_host) *iters_host = std::min(it, (int)max_iters);
     return converged ? SYMNMF_OK : SYMNMF_W_NOT_CONVERGED;
