@@ -10,6 +10,7 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <atomic>
 #include <chrono>
 #include <cmath>
 #include <cstddef>
@@ -54,7 +55,7 @@ struct ProfEntry {
 };
 struct Prof {
     std::mutex mu;
-    bool on = false;
+    std::atomic<bool> on{false};  // read by launches on any thread
     std::vector<ProfEntry> pending;
     int64_t launches[SYMNMF_PROF_COUNT] = {};
     double ms[SYMNMF_PROF_COUNT] = {};
@@ -73,7 +74,12 @@ struct ProfScope {
     ProfScope(int w, double by, hipStream_t s) : st(s), which(w), bytes(by) {
         Prof& p = prof();
         if (!p.on) return;
-        if (hipEventCreate(&a) != hipSuccess || hipEventCreate(&b) != hipSuccess) {
+        if (hipEventCreate(&a) != hipSuccess) {
+            a = nullptr;
+            return;
+        }
+        if (hipEventCreate(&b) != hipSuccess) {
+            (void)hipEventDestroy(a);
             a = b = nullptr;
             return;
         }
