@@ -276,6 +276,225 @@ __global__ __launch_bounds__(256) void sh_panel_kernel(const float* __restrict__
         }
 }
 
+// ---------------------------------------------------------------------------
+// Wide widths (three or more MFMA tiles, e.g. the probe's 80 columns) are bound
+// by the matrix core, and with one 4-row group per trip the panel kernel has
+// only 1 KiB of S per wave in flight, so MFMA issue waits on memory. The ring
+// variant below moves each wave's S tile and the trip's 4 rows of X straight
+// into a wave-private LDS ring with direct-to-LDS loads (no VGPR destination),
+// kRingDepth trips ahead: 4 KiB of S per wave in flight at four waves per SIMD
+// (80 columns at n = 100 000: 15.9 -> 14.0 ms). Nothing is shared between
+// waves, so there are no barriers; the lanes, operands and accumulation order
+// are the panel kernel's (CW = 1, one group per trip), so results are bitwise
+// equal. Contiguous row splits only.
+constexpr int kRingDepth = 4;
+
+typedef __attribute__((address_space(3))) float* lds_float_ptr;
+
+// 16 bytes per lane from global memory to LDS at byte address m0 + 16 lane.
+// Written as asm so that the compiler does not treat the LDS write as pending
+// on every later LDS read (it would wait for the whole ring); the ring waits
+// for exactly the trip it reads with vmcnt below.
+__device__ __forceinline__ void dma_to_lds16(const float* g, uint32_t lds_byte) {
+    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off"
+                 :
+                 : "s"(lds_byte), "v"(g)
+                 : "memory", "m0");
+}
+
+// s_waitcnt vmcnt(N) (gfx9 encoding: vmcnt bits 3:0 and 15:14; expcnt and
+// lgkmcnt left at their maxima, i.e. not waited for).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+    static_assert(N >= 0 && N < 64, "vmcnt is 6 bits");
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
+    asm volatile("" ::: "memory");
+}
+// s_waitcnt lgkmcnt(0): this wave's LDS reads have returned.
+__device__ __forceinline__ void wait_lgkm0() {
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_waitcnt(15 | (7 << 4) | (0 << 8) | (3 << 14));
+    asm volatile("" ::: "memory");
+}
+
+// X DMA instructions per trip: the trip's 4 X rows are 4 width floats, one
+// 16-byte piece per lane.
+constexpr int sh_ring_xdma(int ncm, int nv) { return (16 * ncm + nv + 63) / 64; }
+
+template <int NCM, int NV>
+__global__ __launch_bounds__(256) void sh_ring_kernel(const float* __restrict__ S, int64_t lds,
+                                                      const float* __restrict__ X, int width,
+                                                      RowPlan rp, float* __restrict__ part,
+                                                      int ldp) {
+    constexpr int WMAX = 16 * NCM + NV;
+    constexpr int NXI = sh_ring_xdma(NCM, NV);
+    constexpr int PER = 1 + NXI;                 // DMA instructions per trip and wave
+    constexpr int SLOT = 256 + 4 * WMAX;         // floats: S tile, then 4 X rows
+    constexpr int D = kRingDepth;
+    constexpr int NV1 = NV > 0 ? NV : 1;
+    __shared__ __attribute__((aligned(16))) float ring[4][D * SLOT];
+    const int n = rp.n;
+    const int ntiles = (n + 255) / 256;
+    const int tile = blockIdx.x % ntiles;
+    const int split = blockIdx.x / ntiles;
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int r = lane >> 4;
+    const int cl = lane & 15;
+    const int colbase = tile * 256 + wave * 64 + 4 * cl;
+    const int c_v = 16 * NCM;
+    const bool tile_full = (tile + 1) * 256 <= n;
+    const int jb = split * rp.rows_per_split;
+    const int je = min(n, jb + rp.rows_per_split);
+    const int ntrips = je > jb ? (je - jb + 3) / 4 : 0;
+    const int xs_floats = 4 * width;
+    const int64_t xcount = (int64_t)n * width;
+    float* myring = ring[wave];
+    const uint32_t ring_byte = (uint32_t)(uintptr_t)(lds_float_ptr)(myring);
+    // a column past n loads a valid address (its value is replaced by zero)
+    const int scol = colbase < n ? colbase : 0;
+
+    // trip t: rows jb + 4 t .. +3 into slot t % D
+    auto issue = [&](int t) {
+        const uint32_t slot_byte = ring_byte + 4u * (uint32_t)((t % D) * SLOT);
+        const int j0 = jb + 4 * t;
+        const int jr = j0 + r;
+        const int64_t j = jr < je ? jr : jb;
+        dma_to_lds16(S + j * lds + scol, slot_byte);
+#pragma unroll
+        for (int i = 0; i < NXI; ++i) {
+            const int f = 256 * i + 4 * lane;  // float offset in the trip's X block
+            const int64_t off = (int64_t)j0 * width + f;
+            const int64_t offc = off + 3 < xcount ? off : 0;
+            if (f < xs_floats) dma_to_lds16(X + offc, slot_byte + 4u * (uint32_t)(256 + 256 * i));
+        }
+    };
+
+    floatx4 macc[NCM][4];
+    float vacc[4][NV1];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+#pragma unroll
+        for (int ct = 0; ct < NCM; ++ct) macc[ct][q] = floatx4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int c = 0; c < NV; ++c) vacc[q][c] = 0.f;
+    }
+
+#pragma unroll
+    for (int t = 0; t < D; ++t)
+        if (t < ntrips) issue(t);
+    for (int t = 0; t < ntrips; ++t) {
+        // loads complete in issue order: trip t is in LDS once at most the
+        // PER * later instructions of the trips behind it are outstanding
+        const int later = min(D - 1, ntrips - 1 - t);
+        if (later >= 3) wait_vmcnt<PER * 3>();
+        else if (later == 2) wait_vmcnt<PER * 2>();
+        else if (later == 1) wait_vmcnt<PER * 1>();
+        else wait_vmcnt<0>();
+        const float* sl = myring + (t % D) * SLOT;
+        const float* xr = sl + 256 + r * width;
+        float4 sv = *reinterpret_cast<const float4*>(sl + 4 * lane);
+        float a[NCM];
+        float hv[NV1];
+#pragma unroll
+        for (int ct = 0; ct < NCM; ++ct) {
+            const int c = 16 * ct + cl;
+            a[ct] = c < width ? xr[c] : 0.f;
+        }
+#pragma unroll
+        for (int c4 = 0; c4 < NV; c4 += 4) {
+            const float4 v = *reinterpret_cast<const float4*>(xr + c_v + c4);
+            hv[c4] = v.x;
+            hv[c4 + 1] = v.y;
+            hv[c4 + 2] = v.z;
+            hv[c4 + 3] = v.w;
+        }
+        // the slot is read: refill it with trip t + D
+        wait_lgkm0();
+        if (t + D < ntrips) issue(t + D);
+        if (jb + 4 * t + r >= je) {
+#pragma unroll
+            for (int ct = 0; ct < NCM; ++ct) a[ct] = 0.f;
+#pragma unroll
+            for (int c = 0; c < NV; ++c) hv[c] = 0.f;
+        }
+        if (!tile_full) {
+            sv.x = colbase < n ? sv.x : 0.f;
+            sv.y = colbase + 1 < n ? sv.y : 0.f;
+            sv.z = colbase + 2 < n ? sv.z : 0.f;
+            sv.w = colbase + 3 < n ? sv.w : 0.f;
+        }
+        const float s4[4] = {sv.x, sv.y, sv.z, sv.w};
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+#pragma unroll
+            for (int ct = 0; ct < NCM; ++ct) macc[ct][q] = mfma16x16x4(a[ct], s4[q], macc[ct][q]);
+#pragma unroll
+            for (int c = 0; c < NV; ++c) vacc[q][c] = fmaf(s4[q], hv[c], vacc[q][c]);
+        }
+    }
+
+    // the panel kernel's epilogue with CW = 1
+    float* __restrict__ dst = part + (int64_t)split * ((int64_t)n * ldp);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+#pragma unroll
+        for (int c = 0; c < NV; ++c) {
+            float v = vacc[q][c];
+            v += __shfl_xor(v, 16, 64);
+            v += __shfl_xor(v, 32, 64);
+            vacc[q][c] = v;
+        }
+        const int i = colbase + q;
+        if (i < n) {
+            float* row = dst + (int64_t)i * ldp;
+#pragma unroll
+            for (int ct = 0; ct < NCM; ++ct) {
+                const int c0 = 16 * ct + 4 * r;
+                if (c0 < ldp) {
+                    const floatx4 v = macc[ct][q];
+                    *reinterpret_cast<float4*>(row + c0) = float4{v[0], v[1], v[2], v[3]};
+                }
+            }
+            if (NV > 0) {
+                constexpr int per = NV / 4;
+#pragma unroll
+                for (int e = 0; e < per; ++e) {
+                    float v = 0.f;
+#pragma unroll
+                    for (int rr = 0; rr < 4; ++rr)
+                        if (r == rr) v = vacc[q][per * rr + e];
+                    const int c = c_v + per * r + e;
+                    if (c < ldp) row[c] = v;
+                }
+            }
+        }
+    }
+}
+
+// The ring needs X 16-byte aligned (16-byte DMA pieces), a fixed number of X
+// pieces per trip for the shape, and, with vector-ALU columns, float4 reads of
+// them inside each row.
+template <int NCM, int NV>
+static bool sh_ring_fits(const float* X, int width, const RowPlan& rp) {
+    if (rp.blocks != nullptr || rp.rows_per_split % 4 != 0) return false;
+    if ((reinterpret_cast<uintptr_t>(X) % 16) != 0) return false;
+    if ((width + 63) / 64 != sh_ring_xdma(NCM, NV)) return false;
+    if (NV > 0 && (width % 4 != 0 || 16 * NCM + NV > width)) return false;
+    return true;
+}
+
+template <int NCM, int NV>
+static hipError_t launch_sh_ring(const float* S, int64_t lds, const float* X, int width,
+                                 const RowPlan& rp, int nsplit, float* part, int ldp,
+                                 hipStream_t st) {
+    const int ntiles = (rp.n + 255) / 256;
+    hipLaunchKernelGGL((sh_ring_kernel<NCM, NV>), dim3((unsigned)ntiles * (unsigned)nsplit),
+                       dim3(256), 0, st, S, lds, X, width, rp, part, ldp);
+    return hipGetLastError();
+}
+
 template <int NCM, int NV, int CW, int RM>
 static hipError_t launch_sh_t(const float* S, int64_t lds, const float* X, int width,
                               const RowPlan& rp, int nsplit, float* part, int ldp, hipStream_t st) {
@@ -296,6 +515,11 @@ template <int NCM, int NV, int CW>
 static hipError_t launch_sh_any(const float* S, int64_t lds, const float* X, int width,
                                 const RowPlan& rp, int nsplit, float* part, int ldp,
                                 hipStream_t st) {
+    if constexpr (CW == 1) {
+        // matrix-core-bound widths: the ring keeps more of S in flight
+        if (sh_ring_fits<NCM, NV>(X, width, rp))
+            return launch_sh_ring<NCM, NV>(S, lds, X, width, rp, nsplit, part, ldp, st);
+    }
     if (rp.blocks == nullptr)
         return launch_sh_t<NCM, NV, CW, kRowsContiguous>(S, lds, X, width, rp, nsplit, part, ldp, st);
     // sampled row blocks: fit widths only (k <= 64)

@@ -68,6 +68,27 @@ def test_sh_matches_oracle(torch, api, n, k):
     assert abs(tr - trr) <= 1e-5 * abs(trr)
 
 
+# Widths of three or more MFMA tiles stream S through a per-wave LDS ring when
+# H is 16-byte aligned; an H that is not takes the register panel kernel. Both
+# use the same lanes, operands and accumulation order, so they agree bit for
+# bit (n ragged, vector-ALU columns, a last tile wider than the width).
+@pytest.mark.parametrize("n,k", [(777, 52), (1100, 80), (900, 72), (901, 76), (700, 128),
+                                 (4099, 56), (1000, 120)])
+def test_sh_ring_matches_panel_bitwise(torch, api, n, k):
+    S = synth.random_symmetric_nonneg(n, seed=n + 1)
+    H = synth.random_factor(n, k, seed=k + 1, scale=0.5)
+    Sd = S_to_dev(S, torch)
+    Ha = to_dev(H, torch)
+    buf = torch.empty(n * k + 4, dtype=torch.float32, device="cuda")
+    Hm = buf[1:1 + n * k].view(n, k)
+    Hm.copy_(Ha)
+    assert Ha.data_ptr() % 16 == 0 and Hm.data_ptr() % 16 == 4
+    Pa, tra = api.sh(Sd, Ha)
+    Pm, trm = api.sh(Sd, Hm)
+    assert torch.equal(Pa, Pm)
+    assert tra == trm
+
+
 def test_sh_signed_inputs(torch, api):
     # signed H and S (the probe's basis is signed): bound relative to |S||H|
     n, k = 1500, 80
