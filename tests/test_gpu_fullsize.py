@@ -57,6 +57,34 @@ def test_fullsize_sh_rows(big):
     assert abs(tr - float((H.astype(np.float64) * Pg).sum())) <= 1e-9 * abs(tr)
 
 
+def test_fullsize_probe_width_pass(big):
+    """The probe's S.Q pass at width 80 (64 + 16 oversampling) with a signed
+    basis, as the probe runs it (the LDS-ring kernel): sampled rows against the
+    oracle, bounded relative to |S||Q|, and bit for bit against the register
+    panel kernel, which a misaligned Q selects."""
+    torch, api, w, S, fro, rows = big
+    W = 80
+    rng = np.random.default_rng(5)
+    Q = (rng.standard_normal((N, W)) / np.sqrt(N)).astype(np.float32)
+    Qd = to_dev(Q, torch)
+    P, _ = api.sh(S, Qd)
+    Pg = P.cpu().numpy().astype(np.float64)
+    S_rows = oracle.abs_corr_rows(w.X, rows)
+    Pr, _ = oracle.sh_product(S_rows, Q, rows=rows)
+    # bounded relative to |S||Q| (signed terms cancel), as for the small signed
+    # case; the fp32 S and the fixed-order fp32 sums measure ~3e-8 here
+    scale = np.abs(S_rows) @ np.abs(Q.astype(np.float64))
+    err = (np.abs(Pg[rows] - Pr) / scale).max()
+    print(f"probe-width pass: max |P - P_ref| / (|S||Q|) = {err:.2e}")
+    assert err <= 1e-5, err
+    buf = torch.empty(N * W + 4, dtype=torch.float32, device="cuda")
+    Qm = buf[1:1 + N * W].view(N, W)
+    Qm.copy_(Qd)
+    assert Qd.data_ptr() % 16 == 0 and Qm.data_ptr() % 16 == 4
+    Pm, _ = api.sh(S, Qm)
+    assert torch.equal(P, Pm)
+
+
 def test_fullsize_first_step_and_objective(big):
     torch, api, w, S, fro, rows = big
     lr = 0.05
