@@ -270,6 +270,30 @@ def test_fit_block_svrg_multiblock_splits(torch, api, phi0):
     assert ok, a
 
 
+@pytest.mark.parametrize("solver,phi0", [("full", 0.0), ("block_svrg", 0.5)])
+def test_fit_widest_factor(torch, api, solver, phi0):
+    """k = 64, the widest factor the fit takes (four MFMA tiles and no
+    vector-ALU columns in the S.H pass; the sampled pass at that width):
+    60 steps against the oracle."""
+    w = synth.student_factor(n=1536, k=64, T=252, seed=7, min_size=16)
+    S = oracle.abs_corr(w.X).astype(np.float32)
+    S64 = S.astype(np.float64)
+    res = api.fit(S_to_dev(S, torch), 64, solver=solver, phi0=phi0, block_rows=128,
+                  max_iters=60, tol_rel=0.0, seed=4)
+    m = S64.mean()
+    H0 = oracle.init_uniform(w.n, 64, oracle.init_scale_matched(m, 64), 4)
+    ref = oracle.fit_adaptgrow(S64, H0, oracle.default_lr(m, 64), 60,
+                               solver=(oracle.SOLVER_FULL if solver == "full"
+                                       else oracle.SOLVER_BLOCK_SVRG),
+                               phi0=phi0, block_rows=128, tol=0.0, seed=4)
+    fg, fr = np.asarray(res.f_trace), np.asarray(ref["f"])
+    assert len(fg) == len(fr) and np.array_equal(np.isnan(fg), np.isnan(fr))
+    ex = ~np.isnan(fr)
+    assert traj_rel(fg[ex], fr[ex], float((S64 ** 2).sum())).max() <= 1e-3
+    ok, a = labels_agree(res.H.cpu().numpy(), ref["H"])
+    assert ok, a
+
+
 @pytest.mark.parametrize("solver", ["full", "block_svrg"])
 def test_fit_rmsprop_matches_oracle(torch, api, c1, solver):
     """RMSprop's accumulator (rms_decay = 0.9) on the config-1 input, full batch
