@@ -184,6 +184,25 @@ def test_probe_matches_eigvalsh(torch, api, n, seed):
     assert gamma_of(ev, w.k) == pytest.approx(oracle.gap_ratio(ref, w.k), rel=1e-3)
 
 
+def test_probe_widest_subspace(torch, api):
+    """p = 112 (a 128-column subspace, the widest the probe takes) on a matrix
+    with a planted geometric spectrum of mixed signs: the top 112 eigenvalues
+    by magnitude, signs kept, against LAPACK."""
+    n, p, tol = 600, 112, 1e-6
+    rng = np.random.default_rng(21)
+    Q, _ = np.linalg.qr(rng.standard_normal((n, n)))
+    lam = 100.0 * 0.97 ** np.arange(n)
+    lam[2::3] *= -1.0
+    S = ((Q * lam) @ Q.T).astype(np.float32)
+    S = (S + S.T) / 2
+    ev, its, conv = api.spectral_probe(S_to_dev(S, torch), p=p, max_iters=400, tol=tol, seed=3)
+    ref = oracle.top_eigenvalues(S.astype(np.float64), p)
+    err = np.abs(ev - ref) / abs(ref[0])
+    assert conv, its
+    assert err.max() <= 100 * tol, err.max()
+    assert np.array_equal(np.sign(ev), np.sign(ref))
+
+
 def test_probe_rank_deficient_tpdm(torch, api):
     w = synth.workload("tstress_n8192_k24")
     S = oracle.tpdm(w.X, 0.05).astype(np.float32)
