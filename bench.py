@@ -108,7 +108,7 @@ def measured_traffic():
 def main():
     args = parse()
     if args.gpus != 1:
-        print(json.dumps({"error": "this build runs on exactly one GPU; --gpus must be 1",
+        print(json.dumps({"error": "the benchmark runs on one GPU (the path is not sharded across GPUs); --gpus must be 1",
                           "n_gpus": args.gpus}))
         sys.exit(2)
 
