@@ -43,16 +43,19 @@ def parse():
     ap.add_argument("--cpu-rows", type=int, default=4096,
                     help="rows of S.H the CPU oracle computes for its baseline sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0,
+                    help="CPU time the oracle baseline spends on its timed sample")
     ap.add_argument("--seeds", type=int, default=3,
                     help="seeds of the untimed time-to-convergence sweep (|corr| and TPDM); 0 skips it")
     return ap.parse_args()
 
 
-def cpu_baseline(w, k, rows):
+def cpu_baseline(w, k, rows, seconds=10.0):
     """The CPU oracle timed on a bounded sample of one full-batch iteration:
     the S.H product on `rows` rows of S (the oracle builds those rows itself,
     untimed) plus the gradient and AdaGrad update on all n x k entries; scaled
-    to iterations per second of the whole n x n problem."""
+    to iterations per second of the whole n x n problem. Each part repeats
+    until its share of `seconds` of CPU time is spent (at least 3 times)."""
     import numpy as np
 
     import oracle
@@ -67,25 +70,32 @@ def cpu_baseline(w, k, rows):
     mean_est = float(S_rows.mean())
     H = oracle.init_uniform(n, k, oracle.init_scale_matched(mean_est, k), 0)
     lr = oracle.default_lr(mean_est, k)
-    reps = 3
-    t0 = time.perf_counter()
-    for _ in range(reps):
-        P_rows, _ = oracle.sh_product(S_rows, H, rows=np.arange(rows))
-    t_sh = (time.perf_counter() - t0) / reps
+    def repeat(fn, budget):
+        reps, t0 = 0, time.perf_counter()
+        while reps < 3 or time.perf_counter() - t0 < budget:
+            fn()
+            reps += 1
+        return (time.perf_counter() - t0) / reps, reps
+
+    rows_idx = np.arange(rows)
+    P_rows, _ = oracle.sh_product(S_rows, H, rows=rows_idx)
+    t_sh, reps_sh = repeat(lambda: oracle.sh_product(S_rows, H, rows=rows_idx), 0.8 * seconds)
     P = np.zeros((n, k))
     P[:rows] = P_rows
     G = np.zeros_like(H)
-    t0 = time.perf_counter()
-    for _ in range(reps):
+
+    def rest():
         K = H.T @ H
         g = 4.0 * (H @ K - P)
-        Hn, Gn = oracle.adagrad_step(H, G, g, lr)
-        _ = float((H * P).sum()) + float((K * K).sum())
-    t_rest = (time.perf_counter() - t0) / reps
+        oracle.adagrad_step(H, G, g, lr)
+        return float((H * P).sum()) + float((K * K).sum())
+
+    t_rest, reps_rest = repeat(rest, 0.2 * seconds)
     per_iter = t_sh * (n / rows) + t_rest
     return {"value": 1.0 / per_iter, "unit": "iters/s", "cores": int(cores), "kind": "oracle",
-            "sample": (f"S.H on {rows} of {n} rows (fp64 numpy matmul, x{n / rows:.1f}) plus the "
-                       f"full n x k gradient/AdaGrad update; {reps} repetitions each"),
+            "sample": (f"S.H on {rows} of {n} rows (fp64 numpy matmul, x{n / rows:.1f}; "
+                       f"{reps_sh} repetitions, {reps_sh * t_sh:.1f} s) plus the full n x k "
+                       f"gradient/AdaGrad update ({reps_rest} repetitions, {reps_rest * t_rest:.1f} s)"),
             "seconds_per_iter": per_iter}
 
 
@@ -259,7 +269,7 @@ def main():
                                                                    for r in runs]))}
         out["seeds"] = sweep
     if not args.no_cpu_baseline:
-        out["cpu_baseline"] = cpu_baseline(w, k, args.cpu_rows)
+        out["cpu_baseline"] = cpu_baseline(w, k, args.cpu_rows, args.cpu_seconds)
     print(json.dumps(out), flush=True)
 
 
