@@ -52,7 +52,8 @@ def test_labels_empty(torch, api):
 # padded tile for remainders above 8), ragged n, one and two column groups
 SH_CASES = [(1, 1), (5, 2), (300, 4), (301, 12), (333, 14), (64, 16), (257, 8), (520, 20),
             (1000, 24), (600, 30), (1000, 33), (777, 40), (2000, 48), (1023, 56), (900, 64),
-            (1100, 80), (900, 100), (900, 112), (700, 128), (4099, 24), (8192, 24)]
+            (1100, 80), (900, 100), (900, 112), (700, 128), (4099, 24), (8192, 24),
+            (5, 80), (17, 128), (63, 52)]
 
 
 @pytest.mark.parametrize("n,k", SH_CASES)
@@ -73,7 +74,7 @@ def test_sh_matches_oracle(torch, api, n, k):
 # use the same lanes, operands and accumulation order, so they agree bit for
 # bit (n ragged, vector-ALU columns, a last tile wider than the width).
 @pytest.mark.parametrize("n,k", [(777, 52), (1100, 80), (900, 72), (901, 76), (700, 128),
-                                 (4099, 56), (1000, 120)])
+                                 (4099, 56), (1000, 120), (5, 80), (17, 128)])
 def test_sh_ring_matches_panel_bitwise(torch, api, n, k):
     S = synth.random_symmetric_nonneg(n, seed=n + 1)
     H = synth.random_factor(n, k, seed=k + 1, scale=0.5)
