@@ -178,7 +178,9 @@ int symnmf_spectral_probe(const float* S, int64_t n, int64_t lds, int32_t p,
 /* One S.H pass (the dominant product, P1 "Factorization at scale"; P2):
  * P = S H (n x k, fp32) for symmetric S, and tr_host (nullable) receives
  * tr(H^T S H) = sum_i <H_i, P_i> in fp64. The pass streams S once in row
- * panels and uses S = S^T. Requires 1 <= k <= 128. */
+ * panels and uses S = S^T. Requires 1 <= k <= 128. A 16-byte aligned H
+ * lets the pass use its faster kernels (compile-time widths, and for k > 40
+ * a direct-to-LDS ring); the result is bit for bit the same either way. */
 int symnmf_sh(const float* S, int64_t n, int64_t lds, const float* H, int32_t k,
               float* P, double* tr_host, void* ws, size_t ws_bytes, void* hip_stream);
 
