@@ -70,24 +70,24 @@ hipError_t launch_standardize(const float* X, int T, int n, int64_t ldx, float* 
 __global__ __launch_bounds__(256) void tpdm_ranks_kernel(const float* __restrict__ X, int T, int n,
                                                          int64_t ldx, int* __restrict__ R,
                                                          int* __restrict__ hist, int* flags) {
-    const int i = blockIdx.x * blockDim.x + threadIdx.x;
-    if (i >= n) return;
-    bool finite = true;
-    for (int t = 0; t < T; ++t) finite = finite && isfinite(X[(int64_t)t * ldx + i]);
-    if (!finite) {
-        atomicOr(&flags[0], 1);
+    // windows longer than the LDS stage: one thread per (day t, column i); the
+    // column's losses are read from L2 (the same address across the wave)
+    const int nbt = (T + 255) / 256;  // day blocks per column
+    const int i = (int)(blockIdx.x / nbt);
+    const int t = (int)(blockIdx.x % nbt) * 256 + threadIdx.x;
+    if (i >= n || t >= T) return;
+    const float lt = -X[(int64_t)t * ldx + i];
+    if (!isfinite(lt)) {
+        atomicOr(&flags[0], 1);  // the build stops with E_NONFINITE
         return;
     }
-    for (int t = 0; t < T; ++t) {
-        const float lt = -X[(int64_t)t * ldx + i];
-        int rank = 1;
-        for (int s = 0; s < T; ++s) {
-            const float ls = -X[(int64_t)s * ldx + i];
-            rank += (ls < lt) || (ls == lt && s < t);
-        }
-        R[(int64_t)t * n + i] = rank;
-        atomicAdd(&hist[t * (T + 1) + rank], 1);
+    int rank = 1;
+    for (int s = 0; s < T; ++s) {
+        const float ls = -X[(int64_t)s * ldx + i];
+        rank += (ls < lt) || (ls == lt && s < t);
     }
+    R[(int64_t)t * n + i] = rank;
+    atomicAdd(&hist[(int64_t)t * (T + 1) + rank], 1);
 }
 
 // The same ranks with C columns of the window staged in LDS (losses, T x C):
@@ -130,7 +130,7 @@ __global__ __launch_bounds__(256) void tpdm_ranks_lds_kernel(const float* __rest
             rank += (ls < lt) || (ls == lt && sday < t);
         }
         R[(int64_t)t * n + i0 + c] = rank;
-        atomicAdd(&hist[t * (T + 1) + rank], 1);
+        atomicAdd(&hist[(int64_t)t * (T + 1) + rank], 1);
     }
 }
 
@@ -141,8 +141,10 @@ hipError_t launch_tpdm_ranks(const float* X, int T, int n, int64_t ldx, int* R, 
         hipLaunchKernelGGL(tpdm_ranks_lds_kernel, dim3((unsigned)((n + C - 1) / C)), dim3(256),
                            (size_t)T * C * sizeof(float), st, X, T, n, ldx, C, R, hist, flags);
     } else {
-        hipLaunchKernelGGL(tpdm_ranks_kernel, dim3((n + 255) / 256), dim3(256), 0, st, X, T, n,
-                           ldx, R, hist, flags);
+        const int64_t blocks = (int64_t)((T + 255) / 256) * n;
+        if (blocks > INT32_MAX) return hipErrorInvalidValue;
+        hipLaunchKernelGGL(tpdm_ranks_kernel, dim3((unsigned)blocks), dim3(256), 0, st, X, T, n, ldx,
+                           R, hist, flags);
     }
     return hipGetLastError();
 }
@@ -152,31 +154,45 @@ __device__ __forceinline__ double frechet_sq(int R, int T) {
     return -1.0 / log((double)R / (double)(T + 1));
 }
 
-// radius[t] = sqrt(sum_R hist[t][R] x(R)^2) in fp64; the m largest radii (ties
-// to the earlier day) fill sel[0..m) in descending radius. One workgroup.
-__global__ __launch_bounds__(256) void tpdm_select_kernel(const int* __restrict__ hist, int T,
-                                                          int m, double* __restrict__ radius,
-                                                          int* __restrict__ sel) {
-    for (int t = threadIdx.x; t < T; t += 256) {
-        double s = 0.0;
-        for (int Rk = 1; Rk <= T; ++Rk) s += (double)hist[t * (T + 1) + Rk] * frechet_sq(Rk, T);
-        radius[t] = sqrt(s);
+// radius[t] = sqrt(sum_R hist[t][R] x(R)^2) in fp64, one wave per day: lane
+// l sums R = 1 + l, 65 + l, ... in order, then the lanes are folded by a fixed
+// xor tree, so days with equal rank histograms get bitwise equal radii.
+__global__ __launch_bounds__(256) void tpdm_radius_kernel(const int* __restrict__ hist, int T,
+                                                          double* __restrict__ radius) {
+    const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
+    const int lane = threadIdx.x & 63;
+    if (t >= T) return;
+    const int* h = hist + (int64_t)t * (T + 1);
+    double s = 0.0;
+    for (int Rk = 1 + lane; Rk <= T; Rk += 64) {
+        const int c = h[Rk];
+        if (c) s += (double)c * frechet_sq(Rk, T);
     }
-    __syncthreads();
-    for (int t = threadIdx.x; t < T; t += 256) {
-        const double rt = radius[t];
-        int pos = 0;
-        for (int s = 0; s < T; ++s) {
-            const double rs = radius[s];
-            pos += (rs > rt) || (rs == rt && s < t);
-        }
-        if (pos < m) sel[pos] = t;
+    s = wave_sum(s);
+    if (lane == 0) radius[t] = sqrt(s);
+}
+
+// The m largest radii (ties to the earlier day) fill sel[0..m) in descending
+// radius: day t's position is the number of days ranked before it.
+__global__ __launch_bounds__(256) void tpdm_select_kernel(const double* __restrict__ radius, int T,
+                                                          int m, int* __restrict__ sel) {
+    const int t = blockIdx.x * 256 + threadIdx.x;
+    if (t >= T) return;
+    const double rt = radius[t];
+    int pos = 0;
+    for (int s = 0; s < T; ++s) {
+        const double rs = radius[s];
+        pos += (rs > rt) || (rs == rt && s < t);
     }
+    if (pos < m) sel[pos] = t;
 }
 
 hipError_t launch_tpdm_select(const int* hist, int T, int m, double* radius, int* sel,
                               hipStream_t st) {
-    hipLaunchKernelGGL(tpdm_select_kernel, dim3(1), dim3(256), 0, st, hist, T, m, radius, sel);
+    hipLaunchKernelGGL(tpdm_radius_kernel, dim3((unsigned)((T + 3) / 4)), dim3(256), 0, st, hist, T,
+                       radius);
+    hipLaunchKernelGGL(tpdm_select_kernel, dim3((unsigned)((T + 255) / 256)), dim3(256), 0, st,
+                       radius, T, m, sel);
     return hipGetLastError();
 }
 

@@ -170,6 +170,18 @@ def test_build_tpdm_hand_case(torch, api, golden_dir):
     np.testing.assert_allclose(S.cpu().numpy(), hand, rtol=2e-7)
 
 
+# windows longer than the LDS-staged ranking (more than 16 000 days), and one
+# past 46 340 days, where the day x rank histogram's offsets exceed 2^31
+@pytest.mark.parametrize("n,T", [(40, 16001), (8, 46400)])
+def test_build_tpdm_long_window(torch, api, n, T):
+    w = synth.student_factor_stress(n=n, k=2, T=T, seed=3, min_size=4, stress_groups=2)
+    S, fro = api.build_S(to_dev(w.X, torch), "tpdm", tail_frac=0.05)
+    ref = oracle.tpdm(w.X, 0.05)
+    ok, worst = s_close(S.cpu().numpy(), ref)
+    assert ok, worst
+    assert abs(fro - (ref * ref).sum()) <= 1e-5 * (ref * ref).sum()
+
+
 @pytest.mark.parametrize("n,T,seed", [(1000, 60, 0), (333, 252, 1), (8192, 252, 1)])
 def test_build_tpdm(torch, api, n, T, seed):
     w = synth.student_factor_stress(n=n, k=6 if n < 8192 else 24, T=T, seed=seed,
