@@ -42,7 +42,7 @@ extern "C" {
 #endif
 #pragma GCC visibility push(default)
 
-#define SYMNMF_ABI_VERSION 2
+#define SYMNMF_ABI_VERSION 3
 
 enum symnmf_status {
     SYMNMF_OK = 0,
@@ -74,7 +74,8 @@ enum symnmf_op {
     SYMNMF_OP_PROBE = 1,
     SYMNMF_OP_FIT = 2,
     SYMNMF_OP_SH = 3,
-    SYMNMF_OP_KMEANS = 4 /* k_or_p = k */
+    SYMNMF_OP_KMEANS = 4, /* k_or_p = k */
+    SYMNMF_OP_SQ = 5      /* k_or_p = w */
 };
 
 /* u(seed, c) above: the top 24 bits of output c+1 of SplitMix64 (Steele, Lea
@@ -161,8 +162,9 @@ int symnmf_build_S(int kind, const float* X, int64_t T, int64_t n, int64_t ldx,
 
 /* Spectral probe (P1 "Choosing the rank k", "Why this solver"): the p
  * eigenvalues of symmetric S of largest magnitude, by subspace iteration on
- * w = round_up(p + 16, 16) columns. Q0 = 2 u(seed, i*w + c) - 1; each step
- * forms Y = S Q with the S.H kernel, takes the Ritz values of Q^T S Q (fp64
+ * w = max(round_up(p + 16, 16), min(round_up(2p, 16), 128, n rounded down
+ * to 16)) columns. Q0 = 2 u(seed, i*w + c) - 1; each step
+ * forms Y = S Q with symnmf_sq's pass, takes the Ritz values of Q^T S Q (fp64
  * Jacobi on the host) and orthonormalises Y by CholeskyQR2 (fp64 Cholesky on
  * the host). Stops when every one of the top p Ritz values moved by at most
  * tol |theta_1| since the previous step, or after max_iters steps.
@@ -183,6 +185,20 @@ int symnmf_spectral_probe(const float* S, int64_t n, int64_t lds, int32_t p,
  * a direct-to-LDS ring); the result is bit for bit the same either way. */
 int symnmf_sh(const float* S, int64_t n, int64_t lds, const float* H, int32_t k,
               float* P, double* tr_host, void* ws, size_t ws_bytes, void* hip_stream);
+
+/* The spectral probe's product (P1 "Choosing the rank k", "Why this
+ * solver": the top eigenvalues of S): Y = S Q for S n x n (lds, 16-byte
+ * aligned) and Q, Y n x w dense (ld w), 1 <= w <= 128. Rows of S are read as
+ * stored (S need not be symmetric). Computed on the bf16 matrix cores: every
+ * fp32 operand is split exactly into three bf16 parts, x = x1 + x2 + x3, and
+ * the six products x1y1, x1y2, x2y1, x1y3, x2y2, x3y1 accumulate in fp32; the
+ * three dropped products are at most ~2^-23 |x y|, so Y agrees with an fp32
+ * product to fp32 rounding (not bit for bit with symnmf_sh). Exact splitting
+ * needs |S_ij|, |Q_jc| >= ~1e-31 or zero (smaller values lose low bits).
+ * Deterministic: a fixed split of the columns of S and a fixed-order sum.
+ * Errors: E_INVALID, E_WORKSPACE, E_HIP. */
+int symnmf_sq(const float* S, int64_t n, int64_t lds, const float* Q, int32_t w,
+              float* Y, void* ws, size_t ws_bytes, void* hip_stream);
 
 /* SymNMF fit S ~ H H^T, H >= 0 (P1 "Factorizing with SymNMF", "Why this
  * solver"; P2 AdaGrad update and AdaptGrow sketch; P3).

@@ -23,7 +23,7 @@ E_DEGENERATE = -5
 ABSCORR, TPDM = 0, 1
 AUTO, FULL, BLOCK_SVRG = 0, 1, 2
 INIT_UNIFORM, INIT_SCALE_MATCHED, INIT_CALLER = 0, 1, 2
-OP_BUILD_S, OP_PROBE, OP_FIT, OP_SH, OP_KMEANS = 0, 1, 2, 3, 4
+OP_BUILD_S, OP_PROBE, OP_FIT, OP_SH, OP_KMEANS, OP_SQ = 0, 1, 2, 3, 4, 5
 (PROF_SH_FULL, PROF_SH_SAMPLED, PROF_SH_PROBE, PROF_BUILD_GRAM, PROF_UPDATE,
  PROF_SH_KMEANS) = 0, 1, 2, 3, 4, 5
 PROF_NAMES = {
@@ -96,6 +96,8 @@ SIGNATURES = [
       ctypes.POINTER(_I32), _P, ctypes.c_size_t, _P]),
     ("symnmf_sh", ctypes.c_int,
      [_P, _I64, _I64, _P, _I32, _P, ctypes.POINTER(_D), _P, ctypes.c_size_t, _P]),
+    ("symnmf_sq", ctypes.c_int,
+     [_P, _I64, _I64, _P, _I32, _P, _P, ctypes.c_size_t, _P]),
     ("symnmf_fit", ctypes.c_int,
      [_P, _I64, _I64, _I32, ctypes.POINTER(FitParams), ctypes.POINTER(_D), _I32,
       _P, _P, ctypes.POINTER(_D), _I32, ctypes.POINTER(FitReport), _P,

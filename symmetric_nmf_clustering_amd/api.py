@@ -129,6 +129,23 @@ def sh(S: torch.Tensor, H: torch.Tensor):
     return P, tr.value
 
 
+def sq(S: torch.Tensor, Q: torch.Tensor) -> torch.Tensor:
+    """The probe's product Y = S Q on the bf16 matrix cores (three-part split
+    operands, fp32 accumulation)."""
+    n, lds = _S_layout(S)
+    _require_cuda(Q, "Q")
+    if Q.dim() != 2 or Q.shape[0] != n or not Q.is_contiguous() or Q.dtype != torch.float32:
+        raise ValueError("Q must be a contiguous float32 n x w tensor")
+    w = Q.shape[1]
+    Y = torch.empty_like(Q)
+    lib = L.load()
+    ws = workspace(workspace_bytes(L.OP_SQ, n, w), S.device)
+    st = lib.symnmf_sq(_ptr(S), n, lds, _ptr(Q), w, _ptr(Y), _ptr(ws), ws.numel(),
+                       ctypes.c_void_p(_stream_ptr()))
+    L.check(st, "symnmf_sq")
+    return Y
+
+
 @dataclass
 class FitResult:
     H: torch.Tensor

@@ -57,6 +57,22 @@ struct FitDev {
 // rows of the plan are read from X.
 hipError_t launch_sh_panel(const float* S, int64_t lds, const float* X, int width,
                            const RowPlan& rp, int nsplit, float* part, int ldp, hipStream_t st);
+// ---- the probe's S.Q pass on the bf16 matrix cores (k_sq.hip) -------------
+// Q is packed once per pass into the matrix core's B operands (each fp32 value
+// split exactly into three bf16 parts); the pass then writes
+// part[s][i][c] (ld ldp, split stride n*ldp) = sum over the K blocks of split s
+// of S[i][j] Q[j][c], rows of S read directly (no symmetry assumed).
+struct SqPlan {
+    int nt;             // 16-column tiles of Q (width <= 16 nt)
+    int nsplit;         // K splits (every one non-empty)
+    int kb_per_split;   // 32-column K blocks per split
+    size_t packed_bytes;  // size of the packed Q
+};
+SqPlan sq_plan(int n, int width);
+hipError_t launch_sq_pack(const float* Q, int64_t ldq, int n, int width, const SqPlan& p,
+                          void* Qs, hipStream_t st);
+hipError_t launch_sq_split(const float* S, int64_t lds, const void* Qs, int n, int width,
+                           const SqPlan& p, float* part, int ldp, hipStream_t st);
 // D[j][c] = H[j][c] - Ha[j][c] (fp32) for the rows j of the nsel listed row
 // blocks of block_rows rows (the Block-SVRG correction's input); other rows
 // of D are left as they are.

@@ -280,19 +280,45 @@ size_t kmeans_layout(void* ws, int64_t n, int k, KmeansLayout* L) {
     return c.off;
 }
 
+struct SqLayout {
+    void* qs;  // Q packed into the matrix core's B operands
+    float* part;
+};
+size_t sq_layout(void* ws, int64_t n, int width, SqLayout* L) {
+    Carve c(ws);
+    const SqPlan sp = sq_plan((int)n, width);
+    SqLayout l;
+    l.qs = c.take<char>(sp.packed_bytes);
+    l.part = c.take<float>((size_t)sp.nsplit * n * ldp_of(width));
+    if (L) *L = l;
+    return c.off;
+}
+
 struct ProbeLayout {
     float *Q, *Y, *part, *M, *cg_part;
     double* C;
+    void* qs;
 };
-int probe_width(int p) { return (int)round_up(p + 16, 16); }
+// Subspace width: 2p columns (rounded up to 16) where the widest pass (128)
+// and n allow, and never fewer than p + 16. Convergence goes with
+// |lambda_{w+1} / lambda_p| per step, while a pass costs little more at 128
+// columns than at 80 on the bf16 matrix cores, so the wide block converges in
+// less time overall.
+int probe_width(int p, int64_t n) {
+    const int64_t base = round_up(p + 16, 16);
+    const int64_t wide = std::min<int64_t>(round_up(2 * (int64_t)p, 16),
+                                           std::min<int64_t>(kMaxWidth, n / 16 * 16));
+    return (int)std::max(base, wide);
+}
 size_t probe_layout(void* ws, int64_t n, int p, ProbeLayout* L) {
     Carve c(ws);
-    const int w = probe_width(p);
-    FullPlan fp = full_plan((int)n);
+    const int w = probe_width(p, n);
     ProbeLayout l;
+    const SqPlan sp = sq_plan((int)n, w);
     l.Q = c.take<float>((size_t)n * w);
     l.Y = c.take<float>((size_t)n * w);
-    l.part = c.take<float>((size_t)fp.nsplit * n * ldp_of(w));
+    l.part = c.take<float>((size_t)sp.nsplit * n * ldp_of(w));
+    l.qs = c.take<char>(sp.packed_bytes);
     l.M = c.take<float>((size_t)w * w);
     l.cg_part = c.take<float>((size_t)crossgram_blocks((int)n) * w * w);
     l.C = c.take<double>((size_t)w * w);
@@ -409,11 +435,14 @@ size_t symnmf_workspace_bytes(int op, int64_t n, int32_t k_or_p, int64_t T,
             return std::max(build_layout(nullptr, SYMNMF_ABSCORR, T, n, nullptr),
                             build_layout(nullptr, SYMNMF_TPDM, T, n, nullptr));
         case SYMNMF_OP_PROBE:
-            if (k_or_p < 1 || probe_width(k_or_p) > kMaxWidth) return 0;
+            if (k_or_p < 1 || probe_width(k_or_p, n) > kMaxWidth) return 0;
             return probe_layout(nullptr, n, k_or_p, nullptr);
         case SYMNMF_OP_SH:
             if (k_or_p < 1 || k_or_p > kMaxWidth) return 0;
             return sh_layout(nullptr, n, k_or_p, nullptr);
+        case SYMNMF_OP_SQ:
+            if (k_or_p < 1 || k_or_p > kMaxWidth) return 0;
+            return sq_layout(nullptr, n, k_or_p, nullptr);
         case SYMNMF_OP_KMEANS:
             if (k_or_p < 1 || k_or_p > kMaxK || k_or_p > n) return 0;
             return kmeans_layout(nullptr, n, k_or_p, nullptr);
@@ -486,6 +515,27 @@ int symnmf_sh(const float* S, int64_t n, int64_t lds, const float* H, int32_t k,
         HIPCHK(hipMemcpyAsync(tr_host, L.tr_out, sizeof(double), hipMemcpyDeviceToHost, st));
         HIPCHK(hipStreamSynchronize(st));
     }
+    return SYMNMF_OK;
+}
+
+int symnmf_sq(const float* S, int64_t n, int64_t lds, const float* Q, int32_t w, float* Y,
+              void* ws, size_t ws_bytes, void* hip_stream) {
+    if (!S || !Q || !Y || n < 1 || n > INT32_MAX / 2 || w < 1 || w > kMaxWidth || lds < n ||
+        lds % 4 || !aligned(S, 16) || !aligned(Q, 4) || !aligned(Y, 4))
+        return SYMNMF_E_INVALID;
+    const size_t need = sq_layout(nullptr, n, w, nullptr);
+    if (!ws_ok(ws, ws_bytes, need)) return SYMNMF_E_WORKSPACE;
+    SqLayout L;
+    sq_layout(ws, n, w, &L);
+    hipStream_t st = as_stream(hip_stream);
+    const SqPlan sp = sq_plan((int)n, w);
+    const int ldp = ldp_of(w);
+    HIPCHK(launch_sq_pack(Q, w, (int)n, w, sp, L.qs, st));
+    {
+        ProfScope ps(SYMNMF_PROF_SH_PROBE, 4.0 * n * (double)n + 8.0 * n * w, st);
+        HIPCHK(launch_sq_split(S, lds, L.qs, (int)n, w, sp, L.part, ldp, st));
+    }
+    HIPCHK(launch_reduce_partials(L.part, sp.nsplit, (int)n, w, ldp, Y, nullptr, nullptr, st));
     return SYMNMF_OK;
 }
 
@@ -601,7 +651,7 @@ int symnmf_spectral_probe(const float* S, int64_t n, int64_t lds, int32_t p, int
     if (!S || !eigvals_host || n < 1 || n > INT32_MAX / 2 || lds < n || lds % 4 ||
         !aligned(S, 16) || p < 1 || max_iters < 1 || !(tol >= 0.0))
         return SYMNMF_E_INVALID;
-    const int w = probe_width(p);
+    const int w = probe_width(p, n);
     if (w > kMaxWidth || w > n) return SYMNMF_E_INVALID;
     const size_t need = probe_layout(nullptr, n, p, nullptr);
     if (!ws_ok(ws, ws_bytes, need)) return SYMNMF_E_WORKSPACE;
@@ -609,7 +659,7 @@ int symnmf_spectral_probe(const float* S, int64_t n, int64_t lds, int32_t p, int
     probe_layout(ws, n, p, &L);
     hipStream_t st = as_stream(hip_stream);
     const int nn = (int)n;
-    FullPlan fp = full_plan(nn);
+    const SqPlan sp = sq_plan(nn, w);
     const int ldp = ldp_of(w);
     const int nblk = crossgram_blocks(nn);
 
@@ -621,11 +671,12 @@ int symnmf_spectral_probe(const float* S, int64_t n, int64_t lds, int32_t p, int
 
     // One step: Y = S Q and the Rayleigh quotient Q^T Y into L.C, enqueued.
     auto stage = [&]() -> int {
+        HIPCHK(launch_sq_pack(Q, w, nn, w, sp, L.qs, st));
         {
             ProfScope ps(SYMNMF_PROF_SH_PROBE, 4.0 * n * (double)n + 8.0 * n * w, st);
-            HIPCHK(launch_sh_panel(S, lds, Q, w, fp.rp, fp.nsplit, L.part, ldp, st));
+            HIPCHK(launch_sq_split(S, lds, L.qs, nn, w, sp, L.part, ldp, st));
         }
-        HIPCHK(launch_reduce_partials(L.part, fp.nsplit, nn, w, ldp, Y, nullptr, nullptr, st));
+        HIPCHK(launch_reduce_partials(L.part, sp.nsplit, nn, w, ldp, Y, nullptr, nullptr, st));
         HIPCHK(launch_crossgram(Q, Y, nn, w, L.cg_part, nblk, L.C, st));
         return SYMNMF_OK;
     };

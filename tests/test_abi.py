@@ -39,7 +39,7 @@ def test_every_declared_symbol_is_exported():
 
 def test_abi_version_and_status_strings():
     lib = L.load()
-    assert lib.symnmf_abi_version() == 2
+    assert lib.symnmf_abi_version() == 3
     for s in (0, 1, -1, -2, -3, -4, -5):
         assert len(L.status_string(s)) > 0
     assert L.status_string(12345) == "unknown status"
@@ -91,7 +91,9 @@ def test_workspace_is_order_nk(golden_dir):
         sh = lib.symnmf_workspace_bytes(L.OP_SH, n, k, 0, None)
         assert 0 < sh < 40 * n * k * 4 + 2 ** 20   # <= 32 split partials of n x k
         probe = lib.symnmf_workspace_bytes(L.OP_PROBE, n, 64, 0, None)
-        assert 0 < probe < 40 * n * 80 * 4 + 2 ** 22
+        # p = 64 runs on w = 128 columns: <= 32 split partials of n x w, Q, Y and
+        # the packed Q (6 bytes per element)
+        assert 0 < probe < 40 * n * 128 * 4 + 2 ** 22
         km = lib.symnmf_workspace_bytes(L.OP_KMEANS, n, k, 0, None)
         assert 0 < km < 40 * n * k * 4 + 2 ** 20
     # peak device storage of a fit at n = 1e5: the S itself (4 n^2) plus
@@ -101,6 +103,9 @@ def test_workspace_is_order_nk(golden_dir):
     assert total / (n * n) < c["peak_storage_bytes_per_n2"]["trace_formulation"] * 1.01
     assert lib.symnmf_workspace_bytes(L.OP_FIT, n, 65, 0, None) == 0  # k > 64
     assert lib.symnmf_workspace_bytes(L.OP_PROBE, n, 113, 0, None) == 0  # w > 128
+    assert lib.symnmf_workspace_bytes(L.OP_SQ, n, 129, 0, None) == 0     # w > 128
+    # the packed Q (6 bytes per element, 32-row blocks, 16-column tiles) and partials
+    assert lib.symnmf_workspace_bytes(L.OP_SQ, n, 80, 0, None) >= 6 * n * 80
     assert lib.symnmf_workspace_bytes(L.OP_BUILD_S, n, 1, 1, None) == 0  # T < 2
     assert lib.symnmf_workspace_bytes(99, n, 1, 1, None) == 0
     assert lib.symnmf_workspace_bytes(L.OP_KMEANS, n, 65, 0, None) == 0   # k > 64
@@ -129,6 +134,11 @@ def test_invalid_arguments_rejected_before_device_work():
     assert lib.symnmf_sh(FAKE, 100, 100, FAKE, 0, P, None, FAKE, z, None) == L.E_INVALID
     assert lib.symnmf_sh(FAKE, 100, 100, FAKE, 129, P, None, FAKE, z, None) == L.E_INVALID
     assert lib.symnmf_sh(FAKE, 100, 98, FAKE, 8, P, None, FAKE, z, None) == L.E_INVALID
+    assert lib.symnmf_sq(FAKE, 100, 100, FAKE, 0, P, FAKE, z, None) == L.E_INVALID
+    assert lib.symnmf_sq(FAKE, 100, 100, FAKE, 129, P, FAKE, z, None) == L.E_INVALID
+    assert lib.symnmf_sq(FAKE, 100, 98, FAKE, 8, P, FAKE, z, None) == L.E_INVALID     # lds < n
+    assert lib.symnmf_sq(FAKE, 100, 100, None, 8, P, FAKE, z, None) == L.E_INVALID
+    assert lib.symnmf_sq(FAKE, 100, 100, FAKE, 8, P, FAKE, 64, None) == L.E_WORKSPACE
     assert lib.symnmf_labels(None, 10, 3, FAKE, None) == L.E_INVALID
     assert lib.symnmf_labels(FAKE, 0, 3, FAKE, None) == L.OK  # empty input: nothing to do
     km = lib.symnmf_spherical_kmeans

@@ -85,6 +85,28 @@ def test_fullsize_probe_width_pass(big):
     assert torch.equal(P, Pm)
 
 
+@pytest.mark.parametrize("W", [80, 128])
+def test_fullsize_probe_product(big, W):
+    """symnmf_sq, the probe's pass (bf16 matrix cores, exact three-part operand
+    split), at probe widths with a signed basis: sampled rows against the
+    oracle, bounded relative to |S||Q|, and against the fp32 S.H pass."""
+    torch, api, w, S, fro, rows = big
+    rng = np.random.default_rng(W)
+    Q = (rng.standard_normal((N, W)) / np.sqrt(N)).astype(np.float32)
+    Qd = to_dev(Q, torch)
+    Y = api.sq(S, Qd)
+    Yg = Y.cpu().numpy().astype(np.float64)
+    S_rows = oracle.abs_corr_rows(w.X, rows)
+    Yr, _ = oracle.sh_product(S_rows, Q, rows=rows)
+    scale = np.abs(S_rows) @ np.abs(Q.astype(np.float64))
+    err = (np.abs(Yg[rows] - Yr) / scale).max()
+    print(f"probe product w={W}: max |Y - Y_ref| / (|S||Q|) = {err:.2e}")
+    assert err <= 1e-5, err
+    P, _ = api.sh(S, Qd)
+    d = (np.abs(Yg[rows] - P.cpu().numpy()[rows]) / scale).max()
+    assert d <= 1e-5, d
+
+
 def test_fullsize_first_step_and_objective(big):
     torch, api, w, S, fro, rows = big
     lr = 0.05
