@@ -2,7 +2,8 @@
 
 Builds the dense |corr| S of a synthetic returns window on the device, then runs
 ``--passes`` full S.H passes through the C ABI (``symnmf_sh``: the same kernel
-and launch configuration the fit uses for its full-batch steps) and a plain
+and launch configuration the fit uses for its full-batch steps; with ``--op sq``
+the probe's product ``symnmf_sq`` on a signed n x k basis instead) and a plain
 element-wise kernel that reads ``--copy-mib`` MiB and writes as many. Under
 ``rocprofv3 --pmc FETCH_SIZE`` (or ``WRITE_SIZE``) that kernel's per-dispatch
 counter value gives the factor that turns the counter into bytes; the S.H dispatches then give the
@@ -101,6 +102,7 @@ def main(argv=None):
     ap.add_argument("--T", type=int, default=252)
     ap.add_argument("--passes", type=int, default=4)
     ap.add_argument("--copy-mib", type=int, default=4096)
+    ap.add_argument("--op", choices=("sh", "sq"), default="sh")
     args = ap.parse_args(argv)
 
     import numpy as np
@@ -113,14 +115,22 @@ def main(argv=None):
                              min_size=min(64, args.n // args.k))
     X = torch.from_numpy(w.X).cuda()
     S, _ = api.build_S(X, "abscorr")
-    H = torch.from_numpy(synth.random_factor(args.n, args.k, seed=0, scale=0.1)).cuda()
+    if args.op == "sh":
+        H = torch.from_numpy(synth.random_factor(args.n, args.k, seed=0, scale=0.1)).cuda()
+    else:
+        rng = np.random.default_rng(0)
+        H = torch.from_numpy((rng.standard_normal((args.n, args.k)) / np.sqrt(args.n))
+                             .astype(np.float32)).cuda()
     api.profile_reset()
     api.profile_enable(True)
     for _ in range(args.passes):
-        api.sh(S, H)
+        if args.op == "sh":
+            api.sh(S, H)
+        else:
+            api.sq(S, H)
     torch.cuda.synchronize()
     api.profile_enable(False)
-    sh = api.profile_read(_lib.PROF_SH_FULL)
+    sh = api.profile_read(_lib.PROF_SH_FULL if args.op == "sh" else _lib.PROF_SH_PROBE)
     # calibration: an element-wise kernel that reads copy_mib MiB and writes
     # copy_mib MiB (a contiguous copy_() would go to a DMA engine instead)
     nfl = args.copy_mib * (1 << 20) // 4
@@ -135,7 +145,7 @@ def main(argv=None):
     torch.cuda.synchronize()
     copy_ms = e0.elapsed_time(e1) / COPY_REPS
     ms = sh["ms"] / max(1, sh["launches"])
-    out = {"n": args.n, "k": args.k, "passes": sh["launches"], "sh_avg_ms": ms,
+    out = {"n": args.n, "k": args.k, "op": args.op, "passes": sh["launches"], "sh_avg_ms": ms,
            "sh_GBs": sh["bytes"] / max(1, sh["launches"]) / (ms * 1e-3) / 1e9,
            "copy_bytes_each_way": nfl * 4, "copy_reps": COPY_REPS, "copy_avg_ms": copy_ms,
            "copy_GBs_read_plus_write": 2 * nfl * 4 / (copy_ms * 1e-3) / 1e9}
