@@ -40,6 +40,7 @@ __all__ = [
     "default_lr", "sh_product", "objective_explicit", "objective_trace", "gradient",
     "adagrad_step", "rmsprop_step", "fit_full", "sample_blocks", "svrg_sh_estimate",
     "gap_ratio", "initial_blocks", "fit_adaptgrow", "top_eigenvalues",
+    "subspace_top_eigenvalues",
     "ari_drift", "calm_windows", "control_limit", "cross_block_means", "rolling_fit",
     "spherical_kmeans", "boundary_fraction",
     "labels", "ari", "ari_pairs", "SOLVER_AUTO", "SOLVER_FULL",
@@ -421,6 +422,30 @@ def top_eigenvalues(S, p):
     w = np.linalg.eigvalsh(np.asarray(S, dtype=np.float64))
     order = np.argsort(-np.abs(w), kind="stable")
     return w[order[:p]]
+
+
+def subspace_top_eigenvalues(matmat, n, m, iters, seed=0):
+    """Eigenvalues of largest |lambda| of a symmetric n x n operator known only
+    through its products with n x m blocks (``matmat(V) -> S V``), for sizes
+    where S cannot be factorised whole: fp64 subspace iteration, V <- qr(S V)
+    ``iters`` times from a seeded Gaussian block, then Rayleigh-Ritz on the
+    last basis (P1 "Choosing the rank k": the leading eigenvalues of S).
+
+    Returns (theta, resid): the m Ritz values in descending |theta| with the
+    sign kept, and resid_i = ||S v_i - theta_i v_i||_2 for the unit Ritz
+    vector v_i (an eigenvalue lies within resid_i of theta_i)."""
+    rng = np.random.default_rng(seed)
+    V = np.linalg.qr(rng.standard_normal((n, m)))[0]
+    for _ in range(iters):
+        V = np.linalg.qr(matmat(V))[0]
+    Y = matmat(V)
+    T = V.T @ Y
+    T = 0.5 * (T + T.T)
+    theta, U = np.linalg.eigh(T)
+    order = np.argsort(-np.abs(theta), kind="stable")
+    theta, U = theta[order], U[:, order]
+    resid = np.linalg.norm(Y @ U - (V @ U) * theta, axis=0)
+    return theta, resid
 
 
 # --------------------------------------------------------------------------
