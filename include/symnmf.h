@@ -165,8 +165,8 @@ int symnmf_build_S(int kind, const float* X, int64_t T, int64_t n, int64_t ldx,
  * w = max(round_up(p + 16, 16), min(round_up(2p, 16), 128, n rounded down
  * to 16)) columns. Q0 = 2 u(seed, i*w + c) - 1; each step
  * forms Y = S Q with symnmf_sq's pass, takes the Ritz values of Q^T S Q (fp64
- * Jacobi on the host) and orthonormalises Y by CholeskyQR2 (fp64 Cholesky on
- * the host). Stops when every one of the top p Ritz values moved by at most
+ * Householder tridiagonalisation and implicit QR on the host) and
+ * orthonormalises Y by CholeskyQR2 (fp64 Cholesky on the host). Stops when every one of the top p Ritz values moved by at most
  * tol |theta_1| since the previous step, or after max_iters steps.
  * eigvals_host[p] receives the values in descending |lambda| with the sign
  * kept; iters_host (nullable) the steps taken. Requires 1 <= p and

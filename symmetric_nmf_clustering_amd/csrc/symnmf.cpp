@@ -13,6 +13,7 @@
 #include <atomic>
 #include <chrono>
 #include <cmath>
+#include <limits>
 #include <cstddef>
 #include <cstring>
 #include <mutex>
@@ -202,6 +203,81 @@ void jacobi_eig(int w, std::vector<double>& A, std::vector<double>& ev, std::vec
     }
     ev.resize(w);
     for (int i = 0; i < w; ++i) ev[i] = A[(size_t)i * w + i];
+}
+
+// Eigenvalues of a symmetric w x w matrix A (row-major, destroyed): Householder
+// reduction to tridiagonal form, then implicit symmetric QR steps with
+// Wilkinson shifts and deflation (Golub and Van Loan, "Matrix Computations",
+// Algorithms 8.3.1 and 8.3.2). O(w^3) once, then O(w) per QR step.
+void sym_eigvals(int w, std::vector<double>& A, std::vector<double>& ev) {
+    auto at = [&](int i, int j) -> double& { return A[(size_t)i * w + j]; };
+    std::vector<double> v(w), p(w);
+    for (int k = 0; k + 2 < w; ++k) {
+        const int m = w - k - 1;  // entries k+1 .. w-1 of column k
+        double xn2 = 0.0;
+        for (int i = 0; i < m; ++i) xn2 += at(k + 1 + i, k) * at(k + 1 + i, k);
+        const double xn = std::sqrt(xn2);
+        if (xn == 0.0) continue;
+        const double x0 = at(k + 1, k);
+        const double alpha = x0 >= 0.0 ? -xn : xn;
+        for (int i = 0; i < m; ++i) v[i] = at(k + 1 + i, k);
+        v[0] -= alpha;
+        double vtv = 0.0;
+        for (int i = 0; i < m; ++i) vtv += v[i] * v[i];
+        if (vtv == 0.0) continue;
+        const double beta = 2.0 / vtv;
+        // p = beta B v for the trailing block B = A[k+1.., k+1..]
+        double vtp = 0.0;
+        for (int i = 0; i < m; ++i) {
+            double s = 0.0;
+            for (int j = 0; j < m; ++j) s += at(k + 1 + i, k + 1 + j) * v[j];
+            p[i] = beta * s;
+            vtp += v[i] * p[i];
+        }
+        const double gam = 0.5 * beta * vtp;
+        for (int i = 0; i < m; ++i) p[i] -= gam * v[i];  // q
+        for (int i = 0; i < m; ++i)
+            for (int j = 0; j < m; ++j) at(k + 1 + i, k + 1 + j) -= v[i] * p[j] + p[i] * v[j];
+        at(k + 1, k) = at(k, k + 1) = alpha;
+        for (int i = 1; i < m; ++i) at(k + 1 + i, k) = at(k, k + 1 + i) = 0.0;
+    }
+    std::vector<double> d(w), e(w, 0.0);
+    for (int i = 0; i < w; ++i) d[i] = at(i, i);
+    for (int i = 0; i + 1 < w; ++i) e[i] = at(i + 1, i);
+    const double eps = std::numeric_limits<double>::epsilon();
+    int hi = w - 1, guard = 0;
+    while (hi > 0 && guard < 64 * w) {
+        if (std::fabs(e[hi - 1]) <= eps * (std::fabs(d[hi - 1]) + std::fabs(d[hi]))) {
+            e[hi - 1] = 0.0;
+            --hi;
+            continue;
+        }
+        int lo = hi - 1;
+        while (lo > 0 && std::fabs(e[lo - 1]) > eps * (std::fabs(d[lo - 1]) + std::fabs(d[lo]))) --lo;
+        ++guard;
+        // Wilkinson shift: the eigenvalue of the trailing 2 x 2 closer to d[hi]
+        const double a = d[hi - 1], b = e[hi - 1], c = d[hi];
+        const double delta = 0.5 * (a - c);
+        const double sg = delta >= 0.0 ? 1.0 : -1.0;
+        const double mu = c - b * b / (delta + sg * std::hypot(delta, b));
+        double x = d[lo] - mu, z = e[lo];
+        for (int k = lo; k < hi; ++k) {
+            const double r = std::hypot(x, z);
+            const double cs = r == 0.0 ? 1.0 : x / r, sn = r == 0.0 ? 0.0 : z / r;
+            if (k > lo) e[k - 1] = r;
+            const double dk = d[k], ek = e[k], dk1 = d[k + 1];
+            d[k] = cs * cs * dk + 2.0 * cs * sn * ek + sn * sn * dk1;
+            d[k + 1] = sn * sn * dk - 2.0 * cs * sn * ek + cs * cs * dk1;
+            e[k] = cs * sn * (dk1 - dk) + (cs * cs - sn * sn) * ek;
+            if (k + 1 < hi) {
+                const double f = e[k + 1];
+                z = sn * f;
+                e[k + 1] = cs * f;
+                x = e[k];
+            }
+        }
+    }
+    ev = d;
 }
 
 // G = R^T R with R upper triangular; false on a pivot below rel * G_jj.
@@ -704,7 +780,7 @@ int symnmf_spectral_probe(const float* S, int64_t n, int64_t lds, int32_t p, int
             if ((rc = stage())) return rc;
         }
         std::vector<double> A = T;
-        jacobi_eig(w, A, ev, nullptr);
+        sym_eigvals(w, A, ev);
         std::vector<int> order(w);
         for (int i = 0; i < w; ++i) order[i] = i;
         std::stable_sort(order.begin(), order.end(),
