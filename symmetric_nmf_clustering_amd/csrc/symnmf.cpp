@@ -280,33 +280,46 @@ void sym_eigvals(int w, std::vector<double>& A, std::vector<double>& ev) {
     ev = d;
 }
 
-// G = R^T R with R upper triangular; false on a pivot below rel * G_jj.
-bool cholesky_upper(int w, const std::vector<double>& G, std::vector<double>& R, double rel) {
-    R.assign((size_t)w * w, 0.0);
+// sum_{k < len} a[k] b[k] with four interleaved partial sums (fixed order).
+inline double dot4(const double* a, const double* b, int len) {
+    double s0 = 0.0, s1 = 0.0, s2 = 0.0, s3 = 0.0;
+    int k = 0;
+    for (; k + 4 <= len; k += 4) {
+        s0 += a[k] * b[k];
+        s1 += a[k + 1] * b[k + 1];
+        s2 += a[k + 2] * b[k + 2];
+        s3 += a[k + 3] * b[k + 3];
+    }
+    for (; k < len; ++k) s0 += a[k] * b[k];
+    return (s0 + s1) + (s2 + s3);
+}
+
+// G = L L^T with L lower triangular (row-major, so every inner product below
+// runs over contiguous memory); false on a pivot below rel * G_jj.
+bool cholesky_lower(int w, const std::vector<double>& G, std::vector<double>& L, double rel) {
+    L.assign((size_t)w * w, 0.0);
     for (int j = 0; j < w; ++j) {
-        double d = G[(size_t)j * w + j];
-        for (int i = 0; i < j; ++i) d -= R[(size_t)i * w + j] * R[(size_t)i * w + j];
+        const double* Lj = &L[(size_t)j * w];
+        const double d = G[(size_t)j * w + j] - dot4(Lj, Lj, j);
         if (!(d > rel * G[(size_t)j * w + j]) || !std::isfinite(d)) return false;
-        const double rjj = std::sqrt(d);
-        R[(size_t)j * w + j] = rjj;
-        for (int c = j + 1; c < w; ++c) {
-            double s = G[(size_t)j * w + c];
-            for (int i = 0; i < j; ++i) s -= R[(size_t)i * w + j] * R[(size_t)i * w + c];
-            R[(size_t)j * w + c] = s / rjj;
-        }
+        const double ljj = std::sqrt(d);
+        L[(size_t)j * w + j] = ljj;
+        for (int i = j + 1; i < w; ++i)
+            L[(size_t)i * w + j] = (G[(size_t)i * w + j] - dot4(&L[(size_t)i * w], Lj, j)) / ljj;
     }
     return true;
 }
 
-// inverse of an upper-triangular matrix
-void upper_inverse(int w, const std::vector<double>& R, std::vector<double>& Ri) {
+// Ri = (L^T)^-1 (upper triangular) = (L^-1)^T: row j of Ri is column j of
+// L^-1, by forward substitution on L x = e_j.
+void lower_inverse_transposed(int w, const std::vector<double>& L, std::vector<double>& Ri) {
     Ri.assign((size_t)w * w, 0.0);
-    for (int c = 0; c < w; ++c) {
-        Ri[(size_t)c * w + c] = 1.0 / R[(size_t)c * w + c];
-        for (int r = c - 1; r >= 0; --r) {
-            double s = 0.0;
-            for (int m = r + 1; m <= c; ++m) s += R[(size_t)r * w + m] * Ri[(size_t)m * w + c];
-            Ri[(size_t)r * w + c] = -s / R[(size_t)r * w + r];
+    for (int j = 0; j < w; ++j) {
+        double* x = &Ri[(size_t)j * w];
+        x[j] = 1.0 / L[(size_t)j * w + j];
+        for (int i = j + 1; i < w; ++i) {
+            const double* Li = &L[(size_t)i * w];
+            x[i] = -dot4(Li + j, x + j, i - j) / Li[i];
         }
     }
 }
@@ -684,7 +697,7 @@ namespace {
 // buffers may be swapped).
 int orthonormalize(float*& Y, float*& Q, int n, int w, ProbeLayout& L, hipStream_t st) {
     const int nblk = crossgram_blocks(n);
-    std::vector<double> G((size_t)w * w), R, Ri, V, ev;
+    std::vector<double> G((size_t)w * w), Lf, Ri, V, ev;
     std::vector<float> M((size_t)w * w);
     for (int round = 0; round < 2; ++round) {
         HIPCHK(launch_crossgram(Y, Y, n, w, L.cg_part, nblk, L.C, st));
@@ -697,8 +710,8 @@ int orthonormalize(float*& Y, float*& Q, int n, int w, ProbeLayout& L, hipStream
                 const double s = 0.5 * (G[(size_t)i * w + j] + G[(size_t)j * w + i]);
                 G[(size_t)i * w + j] = G[(size_t)j * w + i] = s;
             }
-        if (cholesky_upper(w, G, R, 1e-10)) {
-            upper_inverse(w, R, Ri);
+        if (cholesky_lower(w, G, Lf, 1e-10)) {
+            lower_inverse_transposed(w, Lf, Ri);
             for (size_t e = 0; e < M.size(); ++e) M[e] = (float)Ri[e];
         } else {
             std::vector<double> A = G;
