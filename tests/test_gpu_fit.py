@@ -203,6 +203,26 @@ def test_probe_widest_subspace(torch, api):
     assert np.array_equal(np.sign(ev), np.sign(ref))
 
 
+@pytest.mark.parametrize("n,p", [(70, 40), (100, 40), (200, 8), (33, 1), (1000, 100)])
+def test_probe_width_rule_edges(torch, api, n, p):
+    """The subspace width at its edges: 2p capped by n (n = 70: 64 = p + 24
+    columns, n = 100: 80), the p + 16 floor (p = 8: 32 columns where 2p is 16;
+    p = 1: 32 of n = 33; p = 100: 128 = p + 28). Planted mixed-sign spectrum
+    against LAPACK."""
+    rng = np.random.default_rng(n + p)
+    Q, _ = np.linalg.qr(rng.standard_normal((n, n)))
+    lam = 50.0 * 0.97 ** np.arange(n)
+    lam[1::4] *= -1.0
+    S = ((Q * lam) @ Q.T).astype(np.float32)
+    S = (S + S.T) / 2
+    tol = 1e-6
+    ev, its, conv = api.spectral_probe(S_to_dev(S, torch), p=p, max_iters=400, tol=tol, seed=1)
+    ref = oracle.top_eigenvalues(S.astype(np.float64), p)
+    assert conv, its
+    assert (np.abs(ev - ref) / abs(ref[0])).max() <= 100 * tol
+    assert np.array_equal(np.sign(ev), np.sign(ref))
+
+
 def test_probe_rank_deficient_tpdm(torch, api):
     w = synth.workload("tstress_n8192_k24")
     S = oracle.tpdm(w.X, 0.05).astype(np.float32)
