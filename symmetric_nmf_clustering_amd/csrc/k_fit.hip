@@ -435,10 +435,96 @@ __global__ __launch_bounds__(256) void crossgram_final_kernel(const float* __res
     if (threadIdx.x == 0) C[idx] = s;
 }
 
-int crossgram_blocks(int n) { return (n + kCgRows - 1) / kCgRows; }
+// Widths that are multiples of 16 (every probe width) run on the matrix core:
+// C = A^T B partials over blocks of kCgRowsM rows with v_mfma_f32_16x16x4_f32
+// (K = 4 rows per step). Wave v owns the 16 x 16 tiles (ti, tj) of C with
+// ti = v, v + 4, ...; lane l = 16 g + m supplies A[row0 + g][16 ti + m] and
+// B[row0 + g][16 tj + m] and holds C[16 ti + 4 g + r][16 tj + m]. Rows past
+// n read row n - 1 and count zero.
+constexpr int kCgRowsM = 512;
+
+template <int NT>
+__global__ __launch_bounds__(256) void crossgram_mfma_kernel(const float* __restrict__ A,
+                                                             const float* __restrict__ B, int n,
+                                                             float* __restrict__ part) {
+    constexpr int w = 16 * NT;
+    constexpr int TI = (NT + 3) / 4;  // tile rows per wave
+    const int lane = threadIdx.x & 63;
+    const int wave = threadIdx.x >> 6;
+    const int g = lane >> 4, m = lane & 15;
+    const int row0 = blockIdx.x * kCgRowsM;
+    const int row1 = min(n, row0 + kCgRowsM);
+    floatx4 acc[TI][NT];
+#pragma unroll
+    for (int a = 0; a < TI; ++a)
+#pragma unroll
+        for (int t = 0; t < NT; ++t) acc[a][t] = floatx4{0.f, 0.f, 0.f, 0.f};
+    for (int r = row0; r < row1; r += 4) {
+        const int row = r + g;
+        const bool ok = row < row1;
+        const int64_t base = (int64_t)(ok ? row : n - 1) * w + m;
+        float av[TI], bv[NT];
+#pragma unroll
+        for (int a = 0; a < TI; ++a) {
+            const int ti = wave + 4 * a;
+            av[a] = (ti < NT && ok) ? A[base + 16 * ti] : 0.f;
+        }
+#pragma unroll
+        for (int t = 0; t < NT; ++t) bv[t] = ok ? B[base + 16 * t] : 0.f;
+#pragma unroll
+        for (int a = 0; a < TI; ++a)
+#pragma unroll
+            for (int t = 0; t < NT; ++t) acc[a][t] = mfma16x16x4(av[a], bv[t], acc[a][t]);
+    }
+    float* out = part + (int64_t)blockIdx.x * w * w;
+#pragma unroll
+    for (int a = 0; a < TI; ++a) {
+        const int ti = wave + 4 * a;
+        if (ti < NT)
+#pragma unroll
+            for (int t = 0; t < NT; ++t)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) out[(16 * ti + 4 * g + r) * w + 16 * t + m] = acc[a][t][r];
+    }
+}
+
+// C[idx] = sum over blocks b in order of part[b][idx] (fp64), one thread per
+// entry, so consecutive threads read consecutive entries of each block.
+__global__ __launch_bounds__(256) void crossgram_fold_kernel(const float* __restrict__ part,
+                                                             int nblk, int ww,
+                                                             double* __restrict__ C) {
+    const int idx = blockIdx.x * 256 + threadIdx.x;
+    if (idx >= ww) return;
+    double s = 0.0;
+    for (int b = 0; b < nblk; ++b) s += (double)part[(int64_t)b * ww + idx];
+    C[idx] = s;
+}
+
+int crossgram_blocks(int n) {
+    return std::max((n + kCgRows - 1) / kCgRows, (n + kCgRowsM - 1) / kCgRowsM);
+}
 
 hipError_t launch_crossgram(const float* A, const float* B, int n, int w, float* part, int nblk,
                             double* C, hipStream_t st) {
+    if (w % 16 == 0 && w <= 128) {
+        const int nb = (n + kCgRowsM - 1) / kCgRowsM;
+        if (nb > nblk) return hipErrorInvalidValue;
+        switch (w / 16) {
+#define CGM_CASE(T)                                                                          \
+    case T:                                                                                  \
+        hipLaunchKernelGGL(crossgram_mfma_kernel<T>, dim3(nb), dim3(256), 0, st, A, B, n, part); \
+        break;
+            CGM_CASE(1) CGM_CASE(2) CGM_CASE(3) CGM_CASE(4) CGM_CASE(5) CGM_CASE(6) CGM_CASE(7)
+            CGM_CASE(8)
+#undef CGM_CASE
+        }
+        hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+        const int ww = w * w;
+        hipLaunchKernelGGL(crossgram_fold_kernel, dim3((ww + 255) / 256), dim3(256), 0, st, part,
+                           nb, ww, C);
+        return hipGetLastError();
+    }
     const int tb = (w + 15) / 16;
     switch (tb) {
 #define CG_CASE(T)                                                                            \
@@ -474,7 +560,61 @@ __global__ __launch_bounds__(256) void rowmat_kernel(const float* __restrict__ Y
         Q[e] = s;
     }
 }
+// Q = Y M on the matrix core for w a multiple of 16: a wave computes 16 rows x
+// all w columns; per 16-column K block lane l = 16 g + m loads Y[row m][16 kb
+// + 4 g .. + 3] as one float4 and runs 4 x NT v_mfma_f32_16x16x4_f32 with B =
+// M[16 kb + 4 g + e][16 t + m] from LDS (M staged once per workgroup).
+template <int NT>
+__global__ __launch_bounds__(256) void rowmat_mfma_kernel(const float* __restrict__ Y,
+                                                          const float* __restrict__ M, int n,
+                                                          float* __restrict__ Q) {
+    constexpr int w = 16 * NT;
+    extern __shared__ float Ms[];
+    for (int e = threadIdx.x; e < w * w; e += 256) Ms[e] = M[e];
+    __syncthreads();
+    const int lane = threadIdx.x & 63;
+    const int wave = threadIdx.x >> 6;
+    const int g = lane >> 4, m = lane & 15;
+    const int row0 = (blockIdx.x * 4 + wave) * 16;
+    if (row0 >= n) return;
+    const float* y = Y + (int64_t)min(row0 + m, n - 1) * w + 4 * g;
+    floatx4 acc[NT];
+#pragma unroll
+    for (int t = 0; t < NT; ++t) acc[t] = floatx4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int kb = 0; kb < NT; ++kb) {
+        const float4 y4 = *reinterpret_cast<const float4*>(y + 16 * kb);
+        const float yv[4] = {y4.x, y4.y, y4.z, y4.w};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const float* mrow = Ms + (16 * kb + 4 * g + e) * w + m;
+#pragma unroll
+            for (int t = 0; t < NT; ++t) acc[t] = mfma16x16x4(yv[e], mrow[16 * t], acc[t]);
+        }
+    }
+#pragma unroll
+    for (int t = 0; t < NT; ++t)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int i = row0 + 4 * g + r;
+            if (i < n) Q[(int64_t)i * w + 16 * t + m] = acc[t][r];
+        }
+}
+
 hipError_t launch_rowmat(const float* Y, const float* M, int n, int w, float* Q, hipStream_t st) {
+    if (w % 16 == 0 && w <= 128 && reinterpret_cast<uintptr_t>(Y) % 16 == 0) {
+        const unsigned blocks = (unsigned)((n + 63) / 64);
+        const size_t shm = (size_t)w * w * sizeof(float);
+        switch (w / 16) {
+#define RM_CASE(T)                                                                             \
+    case T:                                                                                    \
+        hipLaunchKernelGGL(rowmat_mfma_kernel<T>, dim3(blocks), dim3(256), shm, st, Y, M, n, Q); \
+        break;
+            RM_CASE(1) RM_CASE(2) RM_CASE(3) RM_CASE(4) RM_CASE(5) RM_CASE(6) RM_CASE(7) RM_CASE(8)
+#undef RM_CASE
+        }
+        return hipGetLastError();
+    }
     const int64_t total = (int64_t)n * w;
     int64_t blocks = (total + 255) / 256;
     if (blocks > 4096) blocks = 4096;
