@@ -695,10 +695,21 @@ namespace {
 // eigenpairs, which keeps the well-determined directions orthonormal and
 // leaves the null directions near zero. On return `Q` holds the basis (the two
 // buffers may be swapped).
-int orthonormalize(float*& Y, float*& Q, int n, int w, ProbeLayout& L, hipStream_t st) {
+// Host staging of the orthonormalisation's R^-1. Its uploads are
+// asynchronous, so it lives as long as the probe call (each round rewrites it
+// only after a stream synchronisation) and the stream is drained before it
+// goes away, on every return path.
+struct ProbeHostStaging {
+    std::vector<float> M;
+    hipStream_t st;
+    ProbeHostStaging(int w, hipStream_t s) : M((size_t)w * w), st(s) {}
+    ~ProbeHostStaging() { (void)hipStreamSynchronize(st); }
+};
+
+int orthonormalize(float*& Y, float*& Q, int n, int w, ProbeLayout& L, std::vector<float>& M,
+                   hipStream_t st) {
     const int nblk = crossgram_blocks(n);
     std::vector<double> G((size_t)w * w), Lf, Ri, V, ev;
-    std::vector<float> M((size_t)w * w);
     for (int round = 0; round < 2; ++round) {
         HIPCHK(launch_crossgram(Y, Y, n, w, L.cg_part, nblk, L.C, st));
         HIPCHK(hipMemcpyAsync(G.data(), L.C, sizeof(double) * w * w, hipMemcpyDeviceToHost, st));
@@ -725,7 +736,6 @@ int orthonormalize(float*& Y, float*& Q, int n, int w, ProbeLayout& L, hipStream
         }
         HIPCHK(hipMemcpyAsync(L.M, M.data(), sizeof(float) * w * w, hipMemcpyHostToDevice, st));
         HIPCHK(launch_rowmat(Y, L.M, n, w, Q, st));
-        HIPCHK(hipStreamSynchronize(st));  // M's host copy must outlive the transfer
         std::swap(Y, Q);
     }
     std::swap(Y, Q);
@@ -755,7 +765,8 @@ int symnmf_spectral_probe(const float* S, int64_t n, int64_t lds, int32_t p, int
     float* Q = L.Q;
     float* Y = L.Y;
     HIPCHK(launch_init_uniform(Y, (int64_t)n * w, 2.0, -1.0, seed, st));
-    int rc = orthonormalize(Y, Q, nn, w, L, st);
+    ProbeHostStaging staging(w, st);
+    int rc = orthonormalize(Y, Q, nn, w, L, staging.M, st);
     if (rc != SYMNMF_OK) return rc;
 
     // One step: Y = S Q and the Rayleigh quotient Q^T Y into L.C, enqueued.
@@ -788,7 +799,7 @@ int symnmf_spectral_probe(const float* S, int64_t n, int64_t lds, int32_t p, int
         for (double v : T)
             if (!std::isfinite(v)) return SYMNMF_E_NONFINITE;
         if (it < max_iters) {
-            rc = orthonormalize(Y, Q, nn, w, L, st);
+            rc = orthonormalize(Y, Q, nn, w, L, staging.M, st);
             if (rc != SYMNMF_OK) return rc;
             if ((rc = stage())) return rc;
         }
