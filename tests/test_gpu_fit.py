@@ -223,6 +223,18 @@ def test_probe_width_rule_edges(torch, api, n, p):
     assert np.array_equal(np.sign(ev), np.sign(ref))
 
 
+def test_probe_deterministic(torch, api):
+    """Same S, p and seed give bitwise identical eigenvalues and step counts:
+    every sum in the probe (the S.Q split partials, the cross-Grams, the host
+    algebra) runs in a fixed order."""
+    w = synth.workload("blocks_n1024_k8")
+    Sd = S_to_dev(oracle.abs_corr(w.X).astype(np.float32), torch)
+    a = api.spectral_probe(Sd, p=24, max_iters=200, tol=1e-6, seed=4)
+    b = api.spectral_probe(Sd, p=24, max_iters=200, tol=1e-6, seed=4)
+    np.testing.assert_array_equal(a[0], b[0])
+    assert a[1] == b[1] and a[2] == b[2]
+
+
 def test_probe_rank_deficient_tpdm(torch, api):
     w = synth.workload("tstress_n8192_k24")
     S = oracle.tpdm(w.X, 0.05).astype(np.float32)
