@@ -13,9 +13,9 @@
 #include <atomic>
 #include <chrono>
 #include <cmath>
-#include <limits>
 #include <cstddef>
 #include <cstring>
+#include <limits>
 #include <mutex>
 #include <vector>
 
@@ -208,7 +208,8 @@ void jacobi_eig(int w, std::vector<double>& A, std::vector<double>& ev, std::vec
 // Eigenvalues of a symmetric w x w matrix A (row-major, destroyed): Householder
 // reduction to tridiagonal form, then implicit symmetric QR steps with
 // Wilkinson shifts and deflation (Golub and Van Loan, "Matrix Computations",
-// Algorithms 8.3.1 and 8.3.2). O(w^3) once, then O(w) per QR step.
+// Algorithms 8.3.1 and 8.3.2). O(w^3) once, then O(w) per QR step; at most
+// 64 w steps (a few per eigenvalue are the norm).
 void sym_eigvals(int w, std::vector<double>& A, std::vector<double>& ev) {
     auto at = [&](int i, int j) -> double& { return A[(size_t)i * w + j]; };
     std::vector<double> v(w), p(w);
