@@ -141,6 +141,34 @@ def test_fullsize_probe_against_oracle_subspace(big):
     assert abs(fro - fro_o) <= 1e-5 * fro_o  # the library's ||S||^2 from the build
 
 
+def test_fullsize_tpdm_rows_trace_and_spectrum(big):
+    """The TPDM of the same window at n = 100 000 (rank <= m = 13 tail days):
+    sampled rows against the oracle's rows, bitwise symmetry, tr S = 1 (unit
+    angular components, 1/m scaling), and the closed form of its spectrum:
+    the nonzero eigenvalues of Theta^T Theta / m are those of the m x m matrix
+    Theta Theta^T / m, which pins ||S||^2 from the build and the probe's
+    values (the rest of the probe's values are the null space, ~0)."""
+    torch, api, w, S, fro, rows = big
+    St, fro_t = api.build_S(to_dev(w.X, torch), "tpdm")
+    try:
+        theta, _, m = oracle.tpdm_angles(w.X)
+        got = St[torch.from_numpy(rows).cuda()].cpu().numpy()
+        ok, worst = s_close(got, oracle.tpdm_rows(w.X, rows))
+        assert ok, worst
+        assert np.array_equal(got, St[:, torch.from_numpy(rows).cuda()].cpu().numpy().T)
+        assert abs(float(torch.diagonal(St).double().sum()) - 1.0) <= 1e-5
+        lam = np.sort(np.linalg.eigvalsh(theta @ theta.T / m))[::-1]
+        fro_ref = float(np.square(lam).sum())
+        assert abs(fro_t - fro_ref) <= 1e-5 * fro_ref
+        ev, its, conv = api.spectral_probe(St, p=26, max_iters=200, tol=1e-6, seed=0)
+        print(f"TPDM probe: {its} steps, lambda_1 = {ev[0]:.6e} (closed form {lam[0]:.6e})")
+        assert np.all(np.abs(ev[:m] - lam) <= 1e-4 * lam[0])
+        assert np.all(np.abs(ev[m:]) <= 1e-4 * lam[0])
+    finally:
+        del St
+        torch.cuda.empty_cache()
+
+
 def test_fullsize_first_step_and_objective(big):
     torch, api, w, S, fro, rows = big
     lr = 0.05
