@@ -250,7 +250,7 @@ def fit_full(S, H0, lr, max_iters, tol=0.0, eps=1e-8, G0=None, objective="trace"
     S = np.asarray(S, dtype=np.float64)
     H = np.array(H0, dtype=np.float64)
     G = np.zeros_like(H) if G0 is None else np.array(G0, dtype=np.float64)
-    s2 = float((S * S).sum())
+    s2 = float(np.einsum("ij,ij->", S, S))  # ||S||_F^2 without an n x n temporary
     fs = []
     converged = False
     t = 0
@@ -296,9 +296,10 @@ def svrg_sh_estimate(S, H, H_anchor, P_anchor, blocks, block_rows):
     probability |B|/nb and S = S^T; H (H^T H) stays exact."""
     n = S.shape[0]
     nb = -(-n // block_rows)
-    rows = np.concatenate([np.arange(b * block_rows, min(n, (b + 1) * block_rows)) for b in blocks])
-    D = H[rows] - H_anchor[rows]
-    C = S[rows].T @ D
+    C = np.zeros_like(np.asarray(P_anchor, dtype=np.float64))
+    for b in blocks:  # block by block over row slices (views of S), in list order
+        r0, r1 = b * block_rows, min(n, (b + 1) * block_rows)
+        C += S[r0:r1].T @ (H[r0:r1] - H_anchor[r0:r1])
     return P_anchor + (nb / len(blocks)) * C
 
 
@@ -347,7 +348,7 @@ def fit_adaptgrow(S, H0, lr, max_iters, *, solver=SOLVER_AUTO, eigvals=None, k=N
     if k is None:
         k = kk
     G = np.zeros_like(H)
-    s2 = float((S * S).sum())
+    s2 = float(np.einsum("ij,ij->", S, S))  # ||S||_F^2 without an n x n temporary
     nb = -(-n // block_rows)
     gamma = None
     if solver == SOLVER_FULL:
