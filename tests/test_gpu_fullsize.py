@@ -32,6 +32,25 @@ def big():
     torch.cuda.empty_cache()
 
 
+@pytest.fixture(scope="module")
+def oracle_S(big):
+    """The oracle's own fp64 S of the window (80 GB of host memory), built
+    block by block from the returns, and its ||S||_F^2."""
+    import psutil
+    if psutil.virtual_memory().available < 110e9:
+        pytest.skip("needs ~100 GB of free host memory for the oracle's fp64 S")
+    w = big[2]
+    Sh = np.empty((N, N), np.float64)
+    fro_o = 0.0
+    for r0 in range(0, N, 2000):
+        blk = oracle.abs_corr_rows(w.X, np.arange(r0, min(N, r0 + 2000)))
+        Sh[r0:r0 + blk.shape[0]] = blk
+        fro_o += float(np.square(blk).sum())
+        del blk
+    yield Sh, fro_o
+    del Sh
+
+
 def test_fullsize_S_rows_and_symmetry(big):
     torch, api, w, S, fro, rows = big
     got = S[torch.from_numpy(rows).cuda()].cpu().numpy()
@@ -107,31 +126,19 @@ def test_fullsize_probe_product(big, W):
     assert d <= 1e-5, d
 
 
-def test_fullsize_probe_against_oracle_subspace(big):
+def test_fullsize_probe_against_oracle_subspace(big, oracle_S):
     """The probe as the benchmark runs it (p = 64, tol 1e-6, 128 columns)
-    against the oracle's fp64 subspace iteration on its own S, built block by
-    block from the returns window (80 GB of host memory): the 24 planted-factor
-    eigenvalues, which a clear gap separates from the bulk (so 12 oracle steps
-    pin them to their residuals), within the probe's bound; the squares of all
-    64 values below the oracle's ||S||_F^2."""
-    import psutil
-    if psutil.virtual_memory().available < 110e9:
-        pytest.skip("needs ~100 GB of free host memory for the oracle's fp64 S")
+    against the oracle's fp64 subspace iteration on its own S: the 24
+    planted-factor eigenvalues, which a clear gap separates from the bulk (so
+    12 oracle steps pin them to their residuals), within the probe's bound;
+    the squares of all 64 values below the oracle's ||S||_F^2."""
     torch, api, w, S, fro, rows = big
+    Sh, fro_o = oracle_S
     tol = 1e-6
     ev, its, conv = api.spectral_probe(S, p=64, max_iters=400, tol=tol, seed=0)
     assert conv
     print(f"probe: {its} steps, theta_1 = {ev[0]:.6f}")
-    B = 2000
-    Sh = np.empty((N, N), np.float64)
-    fro_o = 0.0
-    for r0 in range(0, N, B):
-        blk = oracle.abs_corr_rows(w.X, np.arange(r0, min(N, r0 + B)))
-        Sh[r0:r0 + blk.shape[0]] = blk
-        fro_o += float(np.square(blk).sum())
-        del blk
     theta, resid = oracle.subspace_top_eigenvalues(lambda V: Sh @ V, N, 32, iters=12, seed=1)
-    del Sh
     lam1 = abs(theta[0])
     assert resid[:24].max() <= 1e-6 * lam1, resid[:24].max()
     err = np.abs(ev[:24] - theta[:24])
@@ -139,6 +146,39 @@ def test_fullsize_probe_against_oracle_subspace(big):
     assert np.all(err <= 100 * tol * lam1 + resid[:24]), err.max() / lam1
     assert float(np.square(ev).sum()) <= fro_o * (1 + 1e-6)
     assert abs(fro - fro_o) <= 1e-5 * fro_o  # the library's ||S||^2 from the build
+
+
+def test_fullsize_block_svrg_two_steps(big, oracle_S):
+    """Block-SVRG as the benchmark starts it (32 of 98 blocks of 1024 rows):
+    an anchor step (exact S H) and a sampled step (the anchor's P plus
+    98/32 times the sampled rows' correction S[B,:]^T (H - H~)[B,:]), every
+    row of H against the oracle's AdaptGrow on its fp64 S. AdaGrad's steps
+    are lr g / sqrt(G): compared where both gradients are decided well above
+    the fp32 noise."""
+    torch, api, w, S, fro, rows = big
+    Sh, fro_o = oracle_S
+    lr, phi0, seed = 0.05, 32.0 / 98.0, 5
+    res = api.fit(S, K, solver="block_svrg", phi0=phi0, init="uniform", init_scale=0.1,
+                  seed=seed, lr=lr, max_iters=2, tol_rel=0.0)
+    assert res.report["blocks_final"] == 32 and res.report["anchors"] == 1
+    H0 = oracle.init_uniform(N, K, 0.1, seed)
+    ref = oracle.fit_adaptgrow(Sh, H0, lr, 2, solver=oracle.SOLVER_BLOCK_SVRG, phi0=phi0,
+                               seed=seed, tol=0.0)
+    assert ref["nsel"] == 32
+    # the two gradients, to mask where a step's sign is decided by rounding
+    P0 = Sh @ H0
+    g0 = 4.0 * (H0 @ (H0.T @ H0) - P0)
+    H1 = np.maximum(H0 - lr * g0 / (np.sqrt(g0 * g0) + 1e-8), 0.0)
+    blocks = oracle.sample_blocks(seed, 1, 98, 32)
+    g1 = 4.0 * (H1 @ (H1.T @ H1) - oracle.svrg_sh_estimate(Sh, H1, H0, P0, blocks, 1024))
+    decided = (np.abs(g0) > 1e-3 * np.abs(g0).max()) & (np.abs(g1) > 1e-3 * np.abs(g1).max())
+    assert decided.mean() > 0.8, decided.mean()
+    H2 = res.H.cpu().numpy().astype(np.float64)
+    err = np.abs(H2 - ref["H"])[decided].max()
+    print(f"Block-SVRG two steps: max |H - H_ref| (decided entries) = {err:.2e}")
+    assert err <= 1e-5, err
+    assert abs(res.f_trace[0] - ref["f"][0]) <= 1e-6 * ref["f"][0]
+    assert np.isnan(res.f_trace[1]) and np.isnan(ref["f"][1])
 
 
 def test_fullsize_tpdm_rows_trace_and_spectrum(big):
