@@ -42,7 +42,7 @@ extern "C" {
 #endif
 #pragma GCC visibility push(default)
 
-#define SYMNMF_ABI_VERSION 3
+#define SYMNMF_ABI_VERSION 4
 
 enum symnmf_status {
     SYMNMF_OK = 0,
@@ -75,7 +75,8 @@ enum symnmf_op {
     SYMNMF_OP_FIT = 2,
     SYMNMF_OP_SH = 3,
     SYMNMF_OP_KMEANS = 4, /* k_or_p = k */
-    SYMNMF_OP_SQ = 5      /* k_or_p = w */
+    SYMNMF_OP_SQ = 5,     /* k_or_p = w */
+    SYMNMF_OP_SH_SYM = 6  /* k_or_p = k */
 };
 
 /* u(seed, c) above: the top 24 bits of output c+1 of SplitMix64 (Steele, Lea
@@ -186,6 +187,22 @@ int symnmf_spectral_probe(const float* S, int64_t n, int64_t lds, int32_t p,
 int symnmf_sh(const float* S, int64_t n, int64_t lds, const float* H, int32_t k,
               float* P, double* tr_host, void* ws, size_t ws_bytes, void* hip_stream);
 
+/* The S.H pass from the upper triangle (P1 "Factorization at scale": the
+ * S H products dominate; P1 "The problem": S is symmetric). Same contract as
+ * symnmf_sh (P = S H, n x k, ld k; tr_host nullable) for 1 <= k <= 32, but
+ * it reads only the 32 x 32 blocks of S on or above the diagonal, each once
+ * (2 n^2 bytes instead of 4 n^2): an off-diagonal block S_ab adds S_ab H_b to
+ * the rows of block a and S_ab^T H_a to the rows of block b. S must be
+ * symmetric; below-diagonal blocks never enter the result, so for a
+ * non-symmetric S it is that of its block-upper mirror (diagonal blocks as
+ * stored). Products run on the bf16
+ * matrix cores with exactly split operands, as symnmf_sq: within fp32
+ * rounding of symnmf_sh, not bit for bit. Deterministic (fixed-order sums of
+ * per-strip and per-chunk partials). S 16-byte aligned, lds % 4 == 0.
+ * Errors: E_INVALID, E_WORKSPACE, E_HIP. */
+int symnmf_sh_sym(const float* S, int64_t n, int64_t lds, const float* H, int32_t k,
+                  float* P, double* tr_host, void* ws, size_t ws_bytes, void* hip_stream);
+
 /* The spectral probe's product (P1 "Choosing the rank k", "Why this
  * solver": the top eigenvalues of S): Y = S Q for S n x n (lds, 16-byte
  * aligned) and Q, Y n x w dense (ld w), 1 <= w <= 128. Rows of S are read as
@@ -275,7 +292,8 @@ enum symnmf_prof_kernel {
     SYMNMF_PROF_BUILD_GRAM = 3, /* the MFMA Z^T Z / Theta^T Theta build        */
     SYMNMF_PROF_UPDATE = 4,     /* fused reduce + gradient + AdaGrad + Gram    */
     SYMNMF_PROF_SH_KMEANS = 5,  /* the spherical k-means passes over S         */
-    SYMNMF_PROF_COUNT = 6
+    SYMNMF_PROF_SH_SYM = 6,     /* the upper-triangle S.H pass (symnmf_sh_sym) */
+    SYMNMF_PROF_COUNT = 7
 };
 void symnmf_profile_enable(int on);
 void symnmf_profile_reset(void);

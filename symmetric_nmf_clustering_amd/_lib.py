@@ -23,12 +23,13 @@ E_DEGENERATE = -5
 ABSCORR, TPDM = 0, 1
 AUTO, FULL, BLOCK_SVRG = 0, 1, 2
 INIT_UNIFORM, INIT_SCALE_MATCHED, INIT_CALLER = 0, 1, 2
-OP_BUILD_S, OP_PROBE, OP_FIT, OP_SH, OP_KMEANS, OP_SQ = 0, 1, 2, 3, 4, 5
+OP_BUILD_S, OP_PROBE, OP_FIT, OP_SH, OP_KMEANS, OP_SQ, OP_SH_SYM = 0, 1, 2, 3, 4, 5, 6
 (PROF_SH_FULL, PROF_SH_SAMPLED, PROF_SH_PROBE, PROF_BUILD_GRAM, PROF_UPDATE,
- PROF_SH_KMEANS) = 0, 1, 2, 3, 4, 5
+ PROF_SH_KMEANS, PROF_SH_SYM) = 0, 1, 2, 3, 4, 5, 6
 PROF_NAMES = {
     PROF_SH_FULL: "sh_full", PROF_SH_SAMPLED: "sh_sampled", PROF_SH_PROBE: "sh_probe",
     PROF_BUILD_GRAM: "build_gram", PROF_UPDATE: "update", PROF_SH_KMEANS: "sh_kmeans",
+    PROF_SH_SYM: "sh_sym",
 }
 
 
@@ -95,6 +96,8 @@ SIGNATURES = [
      [_P, _I64, _I64, _I32, _I32, _D, ctypes.c_uint64, ctypes.POINTER(_D),
       ctypes.POINTER(_I32), _P, ctypes.c_size_t, _P]),
     ("symnmf_sh", ctypes.c_int,
+     [_P, _I64, _I64, _P, _I32, _P, ctypes.POINTER(_D), _P, ctypes.c_size_t, _P]),
+    ("symnmf_sh_sym", ctypes.c_int,
      [_P, _I64, _I64, _P, _I32, _P, ctypes.POINTER(_D), _P, ctypes.c_size_t, _P]),
     ("symnmf_sq", ctypes.c_int,
      [_P, _I64, _I64, _P, _I32, _P, _P, ctypes.c_size_t, _P]),

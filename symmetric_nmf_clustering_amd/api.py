@@ -129,6 +129,25 @@ def sh(S: torch.Tensor, H: torch.Tensor):
     return P, tr.value
 
 
+def sh_sym(S: torch.Tensor, H: torch.Tensor):
+    """The S.H pass from the upper triangle of a symmetric S (each block on or
+    above the diagonal read once, bf16 matrix cores with split operands):
+    returns (P = S H, tr(H^T S H)); k <= 32."""
+    n, lds = _S_layout(S)
+    _require_cuda(H, "H")
+    if H.dim() != 2 or H.shape[0] != n or not H.is_contiguous() or H.dtype != torch.float32:
+        raise ValueError("H must be a contiguous float32 n x k tensor")
+    k = H.shape[1]
+    P = torch.empty_like(H)
+    lib = L.load()
+    ws = workspace(workspace_bytes(L.OP_SH_SYM, n, k), S.device)
+    tr = ctypes.c_double(0.0)
+    st = lib.symnmf_sh_sym(_ptr(S), n, lds, _ptr(H), k, _ptr(P), ctypes.byref(tr), _ptr(ws),
+                           ws.numel(), ctypes.c_void_p(_stream_ptr()))
+    L.check(st, "symnmf_sh_sym")
+    return P, tr.value
+
+
 def sq(S: torch.Tensor, Q: torch.Tensor) -> torch.Tensor:
     """The probe's product Y = S Q on the bf16 matrix cores (three-part split
     operands, fp32 accumulation)."""

@@ -1,14 +1,7 @@
 // The spectral probe's product Y = S Q (P1 "Choosing the rank k", "Why this
 // solver": the leading eigenvalues of S) on the bf16 matrix cores.
 //
-// An fp32 value x splits exactly into three bf16 parts, x = x1 + x2 + x3:
-// x1 = bf16(x) rounded to nearest even, x2 = bf16(x - x1), x3 = bf16(x - x1 -
-// x2). Each difference is exact in fp32, and x's 24-bit significand fits in
-// the three 8-bit ones, so nothing is lost (for |x| above ~1e-31, where x3
-// stays a normal bf16). With |x2| <= 2^-8 |x| and |x3| <= 2^-16 |x|, the
-// product x y keeps the six terms x1y1, x1y2, x2y1, x1y3, x2y2, x3y1; the
-// three it drops sum to at most ~2^-23 |x y|, about one fp32 rounding of the
-// product. Each term is one v_mfma_f32_16x16x32_bf16 accumulating in fp32, so
+// Every fp32 operand is split exactly into three bf16 parts (bf16split.h), so
 // the pass matches an fp32 product to fp32 rounding while its matrix work runs
 // at the bf16 rate: 6 bf16 MFMAs per 32 rows of K against 8 fp32 16x16x4 ones,
 // each 16 times cheaper (2.5 PFLOP/s bf16 against 157.3 TFLOP/s fp32 dense).
@@ -24,50 +17,15 @@
 // the same map, which the Q packing below applies.
 #include <algorithm>
 
+#include "bf16split.h"
 #include "common.h"
 #include "kernels.h"
 
 namespace symnmf {
 namespace {
 
-typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
-typedef float f32x2 __attribute__((ext_vector_type(2)));
-
 constexpr int kSqWaveTiles = 2;                  // 16-row subtiles per wave
 constexpr int kSqTileRows = 4 * 16 * kSqWaveTiles;  // rows of S per workgroup
-
-// (a, b) -> the packed bf16 pairs of their three-part splits (element 0 of a
-// pair in the low half, as the matrix core reads it).
-__device__ __forceinline__ void split3_pair(float a, float b, uint32_t& p1, uint32_t& p2,
-                                            uint32_t& p3) {
-    const f32x2 v = {a, b};
-    const bf16x2 h1 = __builtin_convertvector(v, bf16x2);  // round to nearest even
-    const f32x2 r1 = v - __builtin_convertvector(h1, f32x2);  // exact
-    const bf16x2 h2 = __builtin_convertvector(r1, bf16x2);
-    const f32x2 r2 = r1 - __builtin_convertvector(h2, f32x2);  // exact
-    const bf16x2 h3 = __builtin_convertvector(r2, bf16x2);     // exact
-    p1 = __builtin_bit_cast(uint32_t, h1);
-    p2 = __builtin_bit_cast(uint32_t, h2);
-    p3 = __builtin_bit_cast(uint32_t, h3);
-}
-
-__device__ __forceinline__ void split3_8(const float (&v)[8], u32x4& x1, u32x4& x2, u32x4& x3) {
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-        uint32_t a, b, c;
-        split3_pair(v[2 * q], v[2 * q + 1], a, b, c);
-        x1[q] = a;
-        x2[q] = b;
-        x3[q] = c;
-    }
-}
-
-__device__ __forceinline__ floatx4 mfma_bf16(const u32x4& a, const u32x4& b, floatx4 c) {
-    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
-                                                   __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
-}
 
 // Q (n x width, ld ldq) -> Qs, the B operands of every K block: for block kb,
 // column tile t (16 columns) and part p, 64 lanes x 16 bytes at
@@ -208,13 +166,7 @@ __global__ __launch_bounds__(256) void sq_split_kernel(const float* __restrict__
                 const u32x4 b3 = qs[buf][(3 * t + 2) * 64 + lane];
 #pragma unroll
                 for (int s = 0; s < WM; ++s) {
-                    // smallest terms first
-                    acc[s][t] = mfma_bf16(a3[s], b1, acc[s][t]);
-                    acc[s][t] = mfma_bf16(a2[s], b2, acc[s][t]);
-                    acc[s][t] = mfma_bf16(a1[s], b3, acc[s][t]);
-                    acc[s][t] = mfma_bf16(a2[s], b1, acc[s][t]);
-                    acc[s][t] = mfma_bf16(a1[s], b2, acc[s][t]);
-                    acc[s][t] = mfma_bf16(a1[s], b1, acc[s][t]);
+                    acc[s][t] = mfma_split6(a1[s], a2[s], a3[s], b1, b2, b3, acc[s][t]);
                 }
             }
         }

@@ -384,6 +384,27 @@ size_t sq_layout(void* ws, int64_t n, int width, SqLayout* L) {
     return c.off;
 }
 
+struct SymLayout {
+    void* hs;  // H packed into the matrix core's B operands
+    float* p1;
+    float* p2;
+    double* tr_part;
+    double* tr_out;
+};
+size_t sym_layout(void* ws, int64_t n, int k, SymLayout* L) {
+    Carve c(ws);
+    const SqPlan pk = sq_plan((int)n, k);
+    const SymPlan sp = sym_plan((int)n, k);
+    SymLayout l;
+    l.hs = c.take<char>(pk.packed_bytes);
+    l.p1 = c.take<float>(sp.p1_floats);
+    l.p2 = c.take<float>(sp.p2_floats);
+    l.tr_part = c.take<double>((size_t)cdiv(n, kUpdRows));
+    l.tr_out = c.take<double>(1);
+    if (L) *L = l;
+    return c.off;
+}
+
 struct ProbeLayout {
     float *Q, *Y, *part, *M, *cg_part;
     double* C;
@@ -533,6 +554,9 @@ size_t symnmf_workspace_bytes(int op, int64_t n, int32_t k_or_p, int64_t T,
         case SYMNMF_OP_SQ:
             if (k_or_p < 1 || k_or_p > kMaxWidth) return 0;
             return sq_layout(nullptr, n, k_or_p, nullptr);
+        case SYMNMF_OP_SH_SYM:
+            if (k_or_p < 1 || k_or_p > kSymMaxK) return 0;
+            return sym_layout(nullptr, n, k_or_p, nullptr);
         case SYMNMF_OP_KMEANS:
             if (k_or_p < 1 || k_or_p > kMaxK || k_or_p > n) return 0;
             return kmeans_layout(nullptr, n, k_or_p, nullptr);
@@ -626,6 +650,32 @@ int symnmf_sq(const float* S, int64_t n, int64_t lds, const float* Q, int32_t w,
         HIPCHK(launch_sq_split(S, lds, L.qs, (int)n, w, sp, L.part, ldp, st));
     }
     HIPCHK(launch_reduce_partials(L.part, sp.nsplit, (int)n, w, ldp, Y, nullptr, nullptr, st));
+    return SYMNMF_OK;
+}
+
+int symnmf_sh_sym(const float* S, int64_t n, int64_t lds, const float* H, int32_t k, float* P,
+                  double* tr_host, void* ws, size_t ws_bytes, void* hip_stream) {
+    if (!S || !H || !P || n < 1 || n > INT32_MAX / 2 || k < 1 || k > kSymMaxK || lds < n ||
+        lds % 4 || !aligned(S, 16) || !aligned(H, 4) || !aligned(P, 4))
+        return SYMNMF_E_INVALID;
+    const size_t need = sym_layout(nullptr, n, k, nullptr);
+    if (!ws_ok(ws, ws_bytes, need)) return SYMNMF_E_WORKSPACE;
+    SymLayout L;
+    sym_layout(ws, n, k, &L);
+    hipStream_t st = as_stream(hip_stream);
+    const SqPlan pk = sq_plan((int)n, k);
+    const SymPlan sp = sym_plan((int)n, k);
+    HIPCHK(launch_sq_pack(H, k, (int)n, k, pk, L.hs, st));
+    {
+        ProfScope ps(SYMNMF_PROF_SH_SYM, 2.0 * n * (double)(n + 1) + 8.0 * n * k, st);
+        HIPCHK(launch_sym(S, lds, L.hs, (int)n, k, sp, L.p1, L.p2, st));
+    }
+    HIPCHK(launch_sym_fold(L.p1, L.p2, (int)n, k, sp, P, H, L.tr_part, st));
+    if (tr_host) {
+        HIPCHK(launch_sum_doubles(L.tr_part, cdiv(n, kUpdRows), L.tr_out, st));
+        HIPCHK(hipMemcpyAsync(tr_host, L.tr_out, sizeof(double), hipMemcpyDeviceToHost, st));
+        HIPCHK(hipStreamSynchronize(st));
+    }
     return SYMNMF_OK;
 }
 

@@ -39,7 +39,7 @@ def test_every_declared_symbol_is_exported():
 
 def test_abi_version_and_status_strings():
     lib = L.load()
-    assert lib.symnmf_abi_version() == 3
+    assert lib.symnmf_abi_version() == 4
     for s in (0, 1, -1, -2, -3, -4, -5):
         assert len(L.status_string(s)) > 0
     assert L.status_string(12345) == "unknown status"
@@ -96,6 +96,11 @@ def test_workspace_is_order_nk(golden_dir):
         assert 0 < probe < 40 * n * 128 * 4 + 2 ** 22
         km = lib.symnmf_workspace_bytes(L.OP_KMEANS, n, k, 0, None)
         assert 0 < km < 40 * n * k * 4 + 2 ** 20
+        # the upper-triangle pass: packed H, one row partial per 512-column
+        # strip a row lies in (~n^2 / 1024 rows) and one column partial per
+        # 4096-row chunk: ~k / 1024 of the 4 n^2 bytes of S
+        sym = lib.symnmf_workspace_bytes(L.OP_SH_SYM, n, k, 0, None)
+        assert 0 < sym < 4.0 * n * n * k / 1024 * 1.3 + 40 * n * k * 4 + 2 ** 20
     # peak device storage of a fit at n = 1e5: the S itself (4 n^2) plus
     # workspace well under 1% of it (the pages' ~4 n^2 bytes)
     n = 100000
@@ -104,6 +109,7 @@ def test_workspace_is_order_nk(golden_dir):
     assert lib.symnmf_workspace_bytes(L.OP_FIT, n, 65, 0, None) == 0  # k > 64
     assert lib.symnmf_workspace_bytes(L.OP_PROBE, n, 113, 0, None) == 0  # w > 128
     assert lib.symnmf_workspace_bytes(L.OP_SQ, n, 129, 0, None) == 0     # w > 128
+    assert lib.symnmf_workspace_bytes(L.OP_SH_SYM, n, 33, 0, None) == 0  # k > 32
     # the packed Q (6 bytes per element, 32-row blocks, 16-column tiles) and partials
     assert lib.symnmf_workspace_bytes(L.OP_SQ, n, 80, 0, None) >= 6 * n * 80
     assert lib.symnmf_workspace_bytes(L.OP_BUILD_S, n, 1, 1, None) == 0  # T < 2
@@ -139,6 +145,13 @@ def test_invalid_arguments_rejected_before_device_work():
     assert lib.symnmf_sq(FAKE, 100, 98, FAKE, 8, P, FAKE, z, None) == L.E_INVALID     # lds < n
     assert lib.symnmf_sq(FAKE, 100, 100, None, 8, P, FAKE, z, None) == L.E_INVALID
     assert lib.symnmf_sq(FAKE, 100, 100, FAKE, 8, P, FAKE, 64, None) == L.E_WORKSPACE
+    sym = lib.symnmf_sh_sym
+    assert sym(FAKE, 100, 100, FAKE, 0, P, None, FAKE, z, None) == L.E_INVALID
+    assert sym(FAKE, 100, 100, FAKE, 33, P, None, FAKE, z, None) == L.E_INVALID   # k > 32
+    assert sym(FAKE, 100, 98, FAKE, 8, P, None, FAKE, z, None) == L.E_INVALID     # lds < n
+    assert sym(FAKE, 100, 102, FAKE, 8, P, None, FAKE, z, None) == L.E_INVALID    # lds % 4
+    assert sym(FAKE, 100, 100, None, 8, P, None, FAKE, z, None) == L.E_INVALID
+    assert sym(FAKE, 100, 100, FAKE, 8, P, None, FAKE, 64, None) == L.E_WORKSPACE
     assert lib.symnmf_labels(None, 10, 3, FAKE, None) == L.E_INVALID
     assert lib.symnmf_labels(FAKE, 0, 3, FAKE, None) == L.OK  # empty input: nothing to do
     km = lib.symnmf_spherical_kmeans
