@@ -4,33 +4,39 @@
 // element can serve both of the products it takes part in.
 //
 // S is cut into 32 x 32 blocks; block (a, b) holds rows 32a..32a+31 and
-// columns 32b..32b+31. The pass reads the blocks with a <= b, once each. A
+// columns 32b..32b+31. The pass uses the blocks with a <= b, once each. A
 // block with a < b adds
 //     S_ab H_b     to rows 32a.. of P   (the row side)
 //     S_ab^T H_a   to rows 32b.. of P   (the column side: S_ba = S_ab^T)
 // and a diagonal block adds S_aa H_a only. For a symmetric S that is the full
-// product, summed in another order; the off-diagonal half of S is never read.
+// product, summed in another order; the off-diagonal half of S is not needed.
 //
 // Both sides run on the bf16 matrix cores with exactly split fp32 operands
-// (bf16split.h); H is packed once into B operands (sq_pack_q_kernel), whose K
-// map over the rows of H serves both sides. Row side: lane l holds row l % 16
-// of a 16-row subtile and the 8 columns 4g+e (e < 4), 16+4g+(e-4) (e >= 4),
-// g = l / 16, of the block, straight from global memory (two float4 pieces per
-// row). Column side: the matrix core contracts over the index held within a
-// lane, which here has to be the row, so each wave writes the block's fp32
-// values to an LDS area of its own and reads them back with the column along
-// the lanes and the rows in the same K map.
+// (bf16split.h). A wave owns 64 columns c0..c0+63 and reads a 32-row panel of
+// them as 8 float4 loads: load m gives lane l = 16g + c (g = l / 16) the four
+// columns c0 + 4c + q (q = 0..3) of row 4m + g, so each load instruction reads
+// 256 contiguous bytes of 4 rows (the pattern that streams fastest).
+//  * Column side: for fixed q the panel is a matrix-core B operand as loaded:
+//    column c0 + 4c + q along the lanes, the 32 rows within them (row 4e + g
+//    is element e of lane group g). A = H^T of the panel's rows in that K map
+//    (packed once, "column map"); the result lands as Z[column][factor].
+//  * Row side: the matrix core contracts over the index held within a lane,
+//    which here has to be the column. Multiplying each bf16 part (taken as an
+//    A operand) by a 0/1 selector on the matrix core returns it with the row
+//    along the lanes and 16 consecutive columns within each lane group, exactly
+//    (one nonzero term per output). The 64 columns then form two K blocks,
+//    columns c0 + 16g + 8h + e for half h; H's rows are packed in that map
+//    ("row map"), once per pass.
 //
-// Work: strips of 512 columns (8 waves of 2 blocks), each walked down in
-// chunks of 4096 rows. Workgroup (strip s, chunk q) covers rows
-// [4096 q, min(4096 (q + 1), E_s)), E_s = min(n, 512 (s + 1)): the part of the
-// strip on or above the diagonal. Per 32-row panel the four waves' row-side
-// sums meet in LDS and leave as one partial P1[s][i] per (strip, row); the
-// column side accumulates in registers over the chunk and leaves as
-// P2[q][s][j] per (chunk, column). The fold adds, for row i of strip
-// s(i) = i / 512,
+// Work: strips of 512 columns (8 waves), each walked down in chunks of 4096
+// rows. Workgroup (strip s, chunk qc) covers rows [4096 qc, min(4096 (qc+1),
+// E_s)), E_s = min(n, 512 (s + 1)): the part of the strip on or above the
+// diagonal. Per 32-row panel the eight waves' row-side sums meet in LDS and
+// leave as one partial P1[s][i] per (strip, row); the column side accumulates
+// in registers over the chunk and leaves as P2[qc][s][j] per (chunk, column).
+// The fold adds, for row i of strip s(i) = i / 512,
 //     sum over s = s(i) .. NS-1 of P1[s][i], then
-//     sum over the chunks q of strip s(i) of P2[q][s(i)][i],
+//     sum over the chunks qc of strip s(i) of P2[qc][s(i)][i],
 // in that fixed order, so the result does not depend on timing.
 #include <algorithm>
 
@@ -41,87 +47,124 @@
 namespace symnmf {
 namespace {
 
-constexpr int kSymStripBlocks = kSymStrip / 32;  // 32-column blocks per strip
-constexpr int kSymWaves = 8;                       // waves per workgroup
-constexpr int kSymPitch = 36;  // floats per row of a wave's transpose area (16-byte rows,
-                               // no bank conflicts for the column reads)
+constexpr int kSymWaves = kSymStrip / 64;  // waves per workgroup, 64 columns each
 
 // rows of P1 held by the strips before strip s (each 512 (s' + 1) rows)
 __host__ __device__ inline int64_t p1_rows_before(int s) {
     return (int64_t)(kSymStrip / 2) * s * (s + 1);
 }
 
-template <int NT, int WAVES>
-__global__ __launch_bounds__(64 * WAVES) void sym_kernel(const float* __restrict__ S, int64_t lds,
-                                                  const u32x4* __restrict__ Hs, int n, int k,
-                                                  float* __restrict__ P1, float* __restrict__ P2) {
-    constexpr int WB = kSymStripBlocks / WAVES;  // column blocks per wave
+// (a, b) -> the bf16 pair of two fp32 values that are bf16-exact (their high
+// halves; a in the low half, as the matrix core reads a pair)
+__device__ __forceinline__ uint32_t pack_hi(float a, float b) {
+    return __builtin_amdgcn_perm(__builtin_bit_cast(uint32_t, b), __builtin_bit_cast(uint32_t, a),
+                                 0x07060302u);
+}
+
+// H (n x k, ld k) -> B/A operands of every 32-row K block kb, 16-column tile t
+// and part p at out[((kb * NT + t) * 3 + p) * 64 + l], lane l = 16g + c holding
+// H[row(kb, g, e)][16t + c], e = 0..7, split exactly into three bf16 parts:
+//   column map: row = 32 kb + 4e + g
+//   row map:    row = 64 (kb / 2) + 16g + 8 (kb % 2) + e
+// Rows >= n and columns >= k are zero.
+__global__ __launch_bounds__(256) void sym_pack_kernel(const float* __restrict__ H, int n, int k,
+                                                       int NT, int nkb, int rowmap,
+                                                       u32x4* __restrict__ out) {
+    const int64_t t = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (t >= (int64_t)nkb * NT * 64) return;
+    const int lane = (int)(t & 63);
+    const int64_t kt = t >> 6;
+    const int tile = (int)(kt % NT);
+    const int kb = (int)(kt / NT);
+    const int g = lane >> 4;
+    const int c = 16 * tile + (lane & 15);
+    float v[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+        const int row = rowmap ? 64 * (kb >> 1) + 16 * g + 8 * (kb & 1) + e : 32 * kb + 4 * e + g;
+        v[e] = (row < n && c < k) ? H[(int64_t)row * k + c] : 0.f;
+    }
+    u32x4 x1, x2, x3;
+    split3_8(v, x1, x2, x3);
+    u32x4* dst = out + kt * 3 * 64 + lane;
+    dst[0] = x1;
+    dst[64] = x2;
+    dst[128] = x3;
+}
+
+template <int NT>
+__global__ __launch_bounds__(64 * kSymWaves) void sym_kernel(
+    const float* __restrict__ S, int64_t lds, const u32x4* __restrict__ HsR,
+    const u32x4* __restrict__ HsC, int n, int k, float* __restrict__ P1, float* __restrict__ P2) {
+    constexpr int WAVES = kSymWaves;
     constexpr int NTH = 64 * WAVES;
     constexpr int HB = NT * 3 * 64;  // 16-byte pieces of one packed K block of H
     constexpr int HPER = (HB + NTH - 1) / NTH;
     __shared__ u32x4 hbuf[2][HB];
-    __shared__ __attribute__((aligned(16))) float tbuf[WAVES][32 * kSymPitch];
     __shared__ floatx4 red[2][WAVES][2][NT][64];
 
     const int s = blockIdx.x;
-    const int q = blockIdx.y;
+    const int qc = blockIdx.y;
     const int NS = gridDim.x;
     const int E = min(n, kSymStrip * (s + 1));
-    const int r0 = kSymChunk * q;
+    const int r0 = kSymChunk * qc;
     if (r0 >= E) return;  // the whole workgroup: no barrier is skipped by part of it
     const int r1 = min(E, r0 + kSymChunk);
     const int a0 = r0 >> 5;
     const int a1 = (r1 + 31) >> 5;
     const int nkb = (n + 31) >> 5;
+    const int ngr = (n + 63) >> 6;
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int g = lane >> 4;
     const int lr = lane & 15;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int bw0 = s * kSymStripBlocks + wave * WB;  // first column block of the wave
+    const int c0 = s * kSymStrip + 64 * wave;  // first column of the wave
+    const int b0 = c0 >> 5;                    // its first 32-column block
+    const bool active = c0 < n;
 
-    // row side B operands of the wave's column blocks, kept for the whole chunk
-    u32x4 hj[WB][NT][3];
-    // start of each float4 piece within a row; a piece that would start at
-    // column >= n (ragged last block) reads the row's first 16 bytes instead,
-    // and a block past n reads the last block, so no load sits in a branch;
-    // compute zeroes what lies at columns >= n before use
-    int coff[WB][2];
+    // row side B operands (row map) of the wave's two K blocks, for the chunk
+    u32x4 hj[2][NT][3];
+    {
+        const int G = min(c0 >> 6, ngr - 1);
 #pragma unroll
-    for (int bb = 0; bb < WB; ++bb) {
-        const int kb = min(bw0 + bb, nkb - 1);
+        for (int h = 0; h < 2; ++h)
 #pragma unroll
-        for (int t = 0; t < NT; ++t)
+            for (int t = 0; t < NT; ++t)
 #pragma unroll
-            for (int p = 0; p < 3; ++p) hj[bb][t][p] = Hs[((kb * NT + t) * 3 + p) * 64 + lane];
-#pragma unroll
-        for (int p = 0; p < 2; ++p) {
-            const int col = 32 * kb + 16 * p + 4 * g;
-            coff[bb][p] = col < n ? col : 0;
-        }
+                for (int p = 0; p < 3; ++p)
+                    hj[h][t][p] = HsR[(((2 * G + h) * NT + t) * 3 + p) * 64 + lane];
     }
+    // sel[rho]: picks row 16 rho + lr of a panel in the column map (row 4e + g
+    // is element e of lane group g): bf16 1.0 at element 4 rho + lr / 4 of lane
+    // group lr % 4, zero elsewhere
+    u32x4 sel[2];
+#pragma unroll
+    for (int rho = 0; rho < 2; ++rho)
+#pragma unroll
+        for (int w2 = 0; w2 < 4; ++w2) {
+            const int e = 4 * rho + (lr >> 2);
+            const bool hit = g == (lr & 3) && (e >> 1) == w2;
+            sel[rho][w2] = hit ? (e & 1 ? 0x3F800000u : 0x00003F80u) : 0u;
+        }
+    // a float4 that would start at column >= n (ragged edge, or a wave past n)
+    // reads the row's first 16 bytes instead, so no load sits in a branch; the
+    // values at columns >= n are zeroed before use. A float4 starting below n
+    // lies inside the row (lds is a multiple of 4).
+    const int col = c0 + 4 * lr;
+    const int coff = col < n ? col : 0;
 
-    typedef float Panel[WB][2][8];
-    // panel a: rows 32a + 16 s2 + lr (rows past n read row n - 1, whose
-    // products meet the zero rows of the packed H or are not stored)
+    typedef floatx4 Panel[8];
     auto load = [&](int a, Panel& v) {
 #pragma unroll
-        for (int s2 = 0; s2 < 2; ++s2) {
-            const float* rp = S + (int64_t)min(32 * a + 16 * s2 + lr, n - 1) * lds;
-#pragma unroll
-            for (int bb = 0; bb < WB; ++bb)
-#pragma unroll
-                for (int p = 0; p < 2; ++p) {
-                    const floatx4 t = __builtin_nontemporal_load(
-                        reinterpret_cast<const floatx4*>(rp + coff[bb][p]));
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) v[bb][s2][4 * p + e] = t[e];
-                }
+        for (int m = 0; m < 8; ++m) {
+            const float* rp = S + (int64_t)min(32 * a + 4 * m + g, n - 1) * lds + coff;
+            v[m] = __builtin_nontemporal_load(reinterpret_cast<const floatx4*>(rp));
         }
     };
     u32x4 hst[HPER];
     auto load_h = [&](int a) {
-        const u32x4* src = Hs + (int64_t)min(a, nkb - 1) * HB;
+        const u32x4* src = HsC + (int64_t)min(a, nkb - 1) * HB;
 #pragma unroll
         for (int m = 0; m < HPER; ++m) hst[m] = src[min(tid + NTH * m, HB - 1)];
     };
@@ -133,85 +176,100 @@ __global__ __launch_bounds__(64 * WAVES) void sym_kernel(const float* __restrict
         }
     };
 
-    floatx4 acc2[WB][2][NT];
+    floatx4 acc2[4][NT];
 #pragma unroll
-    for (int bb = 0; bb < WB; ++bb)
+    for (int q = 0; q < 4; ++q)
 #pragma unroll
-        for (int u = 0; u < 2; ++u)
-#pragma unroll
-            for (int t = 0; t < NT; ++t) acc2[bb][u][t] = floatx4{0.f, 0.f, 0.f, 0.f};
-
-    float* __restrict__ tw = tbuf[wave];
+        for (int t = 0; t < NT; ++t) acc2[q][t] = floatx4{0.f, 0.f, 0.f, 0.f};
     const int64_t p1base = p1_rows_before(s);
 
     auto compute = [&](int a, Panel& v) {
         const int hb = a & 1;
-        u32x4 hi[NT][3];
-#pragma unroll
-        for (int t = 0; t < NT; ++t)
-#pragma unroll
-            for (int p = 0; p < 3; ++p) hi[t][p] = hbuf[hb][(3 * t + p) * 64 + lane];
         floatx4 acc1[2][NT];
 #pragma unroll
-        for (int s2 = 0; s2 < 2; ++s2)
+        for (int rho = 0; rho < 2; ++rho)
 #pragma unroll
-            for (int t = 0; t < NT; ++t) acc1[s2][t] = floatx4{0.f, 0.f, 0.f, 0.f};
+            for (int t = 0; t < NT; ++t) acc1[rho][t] = floatx4{0.f, 0.f, 0.f, 0.f};
+        // lanes lr < 8 hold block b0, lanes lr >= 8 block b0 + 1. Row side:
+        // blocks b >= a; column side: blocks b > a. Both skip columns >= n.
+        if (active && a <= b0 + 1) {
+            if (a == b0 + 1 || c0 + 64 > n) {
+                const bool keep_blk = a <= b0 + (lr >> 3);
 #pragma unroll
-        for (int bb = 0; bb < WB; ++bb) {
-            const int b = bw0 + bb;
-            if (b < nkb && a <= b) {
-                if (32 * b + 32 > n) {
+                for (int q = 0; q < 4; ++q) {
+                    const bool keep = keep_blk && col + q < n;
 #pragma unroll
-                    for (int s2 = 0; s2 < 2; ++s2)
-#pragma unroll
-                        for (int e = 0; e < 8; ++e) {
-                            const int jc = 32 * b + (e < 4 ? 4 * g + e : 12 + 4 * g + e);
-                            v[bb][s2][e] = jc < n ? v[bb][s2][e] : 0.f;
-                        }
+                    for (int m = 0; m < 8; ++m) v[m][q] = keep ? v[m][q] : 0.f;
                 }
-                u32x4 x1[2], x2[2], x3[2];
+            }
+            // the parts, as column side B operands: y[q][p] element e of lane
+            // group g = part p of row 4e + g, column c0 + 4 lr + q
+            u32x4 y[4][3];
 #pragma unroll
-                for (int s2 = 0; s2 < 2; ++s2) split3_8(v[bb][s2], x1[s2], x2[s2], x3[s2]);
+            for (int q = 0; q < 4; ++q) {
+                float col8[8];
 #pragma unroll
-                for (int t = 0; t < NT; ++t)
+                for (int m = 0; m < 8; ++m) col8[m] = v[m][q];
+                split3_8(col8, y[q][0], y[q][1], y[q][2]);
+            }
+            if (a <= b0) {
+                const bool ck = a < b0 + (lr >> 3);  // the diagonal block is row side only
+                const u32x4* hl = &hbuf[hb][lane];
 #pragma unroll
-                    for (int s2 = 0; s2 < 2; ++s2)
-                        acc1[s2][t] = mfma_split6(x1[s2], x2[s2], x3[s2], hj[bb][t][0],
-                                                  hj[bb][t][1], hj[bb][t][2], acc1[s2][t]);
-                if (a < b) {
-                    // the block through LDS: written by rows, read by columns
-#pragma unroll
-                    for (int s2 = 0; s2 < 2; ++s2) {
-                        float* rowp = tw + (16 * s2 + lr) * kSymPitch + 4 * g;
-                        *reinterpret_cast<floatx4*>(rowp) =
-                            floatx4{v[bb][s2][0], v[bb][s2][1], v[bb][s2][2], v[bb][s2][3]};
-                        *reinterpret_cast<floatx4*>(rowp + 16) =
-                            floatx4{v[bb][s2][4], v[bb][s2][5], v[bb][s2][6], v[bb][s2][7]};
+                for (int q = 0; q < 4; ++q) {
+                    u32x4 z1 = y[q][0], z2 = y[q][1], z3 = y[q][2];
+                    if (a == b0) {
+                        z1 = ck ? z1 : u32x4{0u, 0u, 0u, 0u};
+                        z2 = ck ? z2 : u32x4{0u, 0u, 0u, 0u};
+                        z3 = ck ? z3 : u32x4{0u, 0u, 0u, 0u};
                     }
-                    float w[2][8];
-#pragma unroll
-                    for (int u = 0; u < 2; ++u)
-#pragma unroll
-                        for (int e = 0; e < 8; ++e) {
-                            const int row = e < 4 ? 4 * g + e : 12 + 4 * g + e;
-                            w[u][e] = tw[row * kSymPitch + 16 * u + lr];
-                        }
-                    u32x4 y1[2], y2[2], y3[2];
-#pragma unroll
-                    for (int u = 0; u < 2; ++u) split3_8(w[u], y1[u], y2[u], y3[u]);
 #pragma unroll
                     for (int t = 0; t < NT; ++t)
+                        acc2[q][t] = mfma_split6(hl[(3 * t) * 64], hl[(3 * t + 1) * 64],
+                                                 hl[(3 * t + 2) * 64], z1, z2, z3, acc2[q][t]);
+                }
+            }
+            // row side, one part at a time (smallest first): the part with the
+            // row along the lanes, then its terms of the six-term product
 #pragma unroll
-                        for (int u = 0; u < 2; ++u)
-                            acc2[bb][u][t] = mfma_split6(y1[u], y2[u], y3[u], hi[t][0], hi[t][1],
-                                                         hi[t][2], acc2[bb][u][t]);
+            for (int p = 2; p >= 0; --p) {
+#pragma unroll
+                for (int rho = 0; rho < 2; ++rho) {
+                    floatx4 d[4];
+#pragma unroll
+                    for (int q = 0; q < 4; ++q)
+                        d[q] = mfma_bf16(y[q][p], sel[rho], floatx4{0.f, 0.f, 0.f, 0.f});
+                    // lane (lr, g') now holds part p of row 32a + 16 rho + lr,
+                    // columns c0 + 16 g' + 4 r + q in d[q][r]; K block h takes
+                    // columns c0 + 16 g' + 8 h + e, e = 4 (r - 2h) + q
+#pragma unroll
+                    for (int h = 0; h < 2; ++h) {
+                        const u32x4 ap = {pack_hi(d[0][2 * h], d[1][2 * h]),
+                                          pack_hi(d[2][2 * h], d[3][2 * h]),
+                                          pack_hi(d[0][2 * h + 1], d[1][2 * h + 1]),
+                                          pack_hi(d[2][2 * h + 1], d[3][2 * h + 1])};
+#pragma unroll
+                        for (int t = 0; t < NT; ++t) {
+                            // the terms a_p b_r with p + r <= 4 (parts numbered 1..3)
+                            if (p == 2) {
+                                acc1[rho][t] = mfma_bf16(ap, hj[h][t][0], acc1[rho][t]);
+                            } else if (p == 1) {
+                                acc1[rho][t] = mfma_bf16(ap, hj[h][t][1], acc1[rho][t]);
+                                acc1[rho][t] = mfma_bf16(ap, hj[h][t][0], acc1[rho][t]);
+                            } else {
+                                acc1[rho][t] = mfma_bf16(ap, hj[h][t][2], acc1[rho][t]);
+                                acc1[rho][t] = mfma_bf16(ap, hj[h][t][1], acc1[rho][t]);
+                                acc1[rho][t] = mfma_bf16(ap, hj[h][t][0], acc1[rho][t]);
+                            }
+                        }
+                    }
                 }
             }
         }
 #pragma unroll
-        for (int s2 = 0; s2 < 2; ++s2)
+        for (int rho = 0; rho < 2; ++rho)
 #pragma unroll
-            for (int t = 0; t < NT; ++t) red[hb][wave][s2][t][lane] = acc1[s2][t];
+            for (int t = 0; t < NT; ++t) red[hb][wave][rho][t][lane] = acc1[rho][t];
     };
 
     // the waves' row-side sums of panel a, in wave order, to P1
@@ -227,11 +285,11 @@ __global__ __launch_bounds__(64 * WAVES) void sym_kernel(const float* __restrict
             const int rr = o / k;
             const int c = o - rr * k;
             const int i = 32 * a + rr;
-            const int s2 = rr >> 4;
+            const int rho = rr >> 4;
             const int gg = (rr >> 2) & 3;
             const int r = rr & 3;
             const int t = c >> 4;
-            const int idx = ((s2 * NT + t) * 64 + 16 * gg + (c & 15)) * 4 + r;
+            const int idx = ((rho * NT + t) * 64 + 16 * gg + (c & 15)) * 4 + r;
             float sum = rf[idx];
 #pragma unroll
             for (int w = 1; w < WAVES; ++w) sum += rf[w * WSTRIDE + idx];
@@ -264,26 +322,22 @@ __global__ __launch_bounds__(64 * WAVES) void sym_kernel(const float* __restrict
         panel(a + 1, vb, va);
     }
 
-    // column side of the chunk: lane l holds columns 16u + 4g + r of each
-    // block, factor column 16t + l % 16
-    float* __restrict__ dst = P2 + ((int64_t)q * NS + s) * kSymStrip * k;
+    // column side of the chunk: lane (lr, g') holds column c0 + 4 lr + q,
+    // factor columns 16t + 4g' + r
+    float* __restrict__ dst = P2 + ((int64_t)qc * NS + s) * kSymStrip * k;
 #pragma unroll
-    for (int bb = 0; bb < WB; ++bb)
+    for (int q = 0; q < 4; ++q)
 #pragma unroll
-        for (int u = 0; u < 2; ++u)
+        for (int t = 0; t < NT; ++t)
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
-                const int jl = (wave * WB + bb) * 32 + 16 * u + 4 * g + r;
-#pragma unroll
-                for (int t = 0; t < NT; ++t) {
-                    const int c = 16 * t + lr;
-                    if (c < k) dst[(int64_t)jl * k + c] = acc2[bb][u][t][r];
-                }
+                const int c = 16 * t + 4 * g + r;
+                if (c < k) dst[(int64_t)(64 * wave + 4 * lr + q) * k + c] = acc2[q][t][r];
             }
 }
 
 // P[i][c] = sum over s >= i / 512 of P1[s][i][c], then over the chunks of
-// strip i / 512 of P2[q][s(i)][i][c]; tr_part[b] = sum over the rows of block
+// strip i / 512 of P2[qc][s(i)][i][c]; tr_part[b] = sum over the rows of block
 // b of <Hdot_i, P_i> (fp64), blocks of kUpdRows rows.
 __global__ __launch_bounds__(256) void sym_fold_kernel(const float* __restrict__ P1,
                                                        const float* __restrict__ P2, int n, int k,
@@ -330,22 +384,39 @@ SymPlan sym_plan(int n, int k) {
     p.nq = (n + kSymChunk - 1) / kSymChunk;
     p.p1_floats = (size_t)(p1_rows_before(p.ns - 1) + n) * k;
     p.p2_floats = (size_t)p.nq * p.ns * kSymStrip * k;
+    p.nkb_col = (n + 31) / 32;
+    p.nkb_row = 2 * ((n + 63) / 64);
+    p.packed_col_bytes = (size_t)p.nkb_col * p.nt * 3 * 64 * 16;
+    p.packed_row_bytes = (size_t)p.nkb_row * p.nt * 3 * 64 * 16;
     return p;
 }
 
-hipError_t launch_sym(const float* S, int64_t lds, const void* Hs, int n, int k,
+hipError_t launch_sym_pack(const float* H, int n, int k, const SymPlan& p, void* HsR, void* HsC,
+                           hipStream_t st) {
+    for (int rowmap = 0; rowmap < 2; ++rowmap) {
+        const int nkb = rowmap ? p.nkb_row : p.nkb_col;
+        const int64_t threads = (int64_t)nkb * p.nt * 64;
+        hipLaunchKernelGGL(sym_pack_kernel, dim3((unsigned)((threads + 255) / 256)), dim3(256), 0,
+                           st, H, n, k, p.nt, nkb, rowmap,
+                           static_cast<u32x4*>(rowmap ? HsR : HsC));
+        const hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
+    return hipSuccess;
+}
+
+hipError_t launch_sym(const float* S, int64_t lds, const void* HsR, const void* HsC, int n, int k,
                       const SymPlan& p, float* P1, float* P2, hipStream_t st) {
-    const u32x4* h = static_cast<const u32x4*>(Hs);
+    const u32x4* hr = static_cast<const u32x4*>(HsR);
+    const u32x4* hc = static_cast<const u32x4*>(HsC);
     const dim3 grid((unsigned)p.ns, (unsigned)p.nq);
     const dim3 block(64 * kSymWaves);
     switch (p.nt) {
         case 1:
-            hipLaunchKernelGGL((sym_kernel<1, kSymWaves>), grid, block, 0, st, S, lds, h, n, k, P1,
-                               P2);
+            hipLaunchKernelGGL((sym_kernel<1>), grid, block, 0, st, S, lds, hr, hc, n, k, P1, P2);
             break;
         case 2:
-            hipLaunchKernelGGL((sym_kernel<2, kSymWaves>), grid, block, 0, st, S, lds, h, n, k, P1,
-                               P2);
+            hipLaunchKernelGGL((sym_kernel<2>), grid, block, 0, st, S, lds, hr, hc, n, k, P1, P2);
             break;
         default: return hipErrorInvalidValue;
     }

@@ -74,25 +74,30 @@ hipError_t launch_sq_pack(const float* Q, int64_t ldq, int n, int width, const S
 hipError_t launch_sq_split(const float* S, int64_t lds, const void* Qs, int n, int width,
                            const SqPlan& p, float* part, int ldp, hipStream_t st);
 // ---- the symmetric S.H pass on the bf16 matrix cores (k_sym.hip) ----------
-// Reads the 32 x 32 blocks of S on or above the diagonal once each; H is
-// packed as the probe packs Q (launch_sq_pack, nt = sym_plan's). The pass
-// writes row-side partials P1 (one per 512-column strip and row, compact:
-// strip s holds rows [0, min(n, 512 (s + 1)))) and column-side partials P2
-// (one per 4096-row chunk, strip and column of the strip); the fold adds them
-// in a fixed order into P (n x k, ld k), with the trace partials as
-// launch_reduce_partials.
+// Uses the 32 x 32 blocks of S on or above the diagonal once each; H is
+// packed twice (launch_sym_pack: the column side's and the row side's K maps).
+// The pass writes row-side partials P1 (one per 512-column strip and row,
+// compact: strip s holds rows [0, min(n, 512 (s + 1)))) and column-side
+// partials P2 (one per 4096-row chunk, strip and column of the strip); the
+// fold adds them in a fixed order into P (n x k, ld k), with the trace
+// partials as launch_reduce_partials.
 constexpr int kSymStrip = 512;   // columns per strip
 constexpr int kSymChunk = 4096;  // rows per chunk
 constexpr int kSymMaxK = 32;     // widest factor of the symmetric pass
 struct SymPlan {
-    int nt;            // 16-column tiles of H
-    int ns;            // strips
-    int nq;            // chunks of the tallest strip
-    size_t p1_floats;  // size of P1
-    size_t p2_floats;  // size of P2
+    int nt;                   // 16-column tiles of H
+    int ns;                   // strips
+    int nq;                   // chunks of the tallest strip
+    size_t p1_floats;         // size of P1
+    size_t p2_floats;         // size of P2
+    int nkb_col, nkb_row;     // K blocks of the two packings of H
+    size_t packed_col_bytes;  // sizes of the two packings
+    size_t packed_row_bytes;
 };
 SymPlan sym_plan(int n, int k);
-hipError_t launch_sym(const float* S, int64_t lds, const void* Hs, int n, int k,
+hipError_t launch_sym_pack(const float* H, int n, int k, const SymPlan& p, void* HsR, void* HsC,
+                           hipStream_t st);
+hipError_t launch_sym(const float* S, int64_t lds, const void* HsR, const void* HsC, int n, int k,
                       const SymPlan& p, float* P1, float* P2, hipStream_t st);
 hipError_t launch_sym_fold(const float* P1, const float* P2, int n, int k, const SymPlan& p,
                            float* P, const float* Hdot, double* tr_part, hipStream_t st);

@@ -385,7 +385,8 @@ size_t sq_layout(void* ws, int64_t n, int width, SqLayout* L) {
 }
 
 struct SymLayout {
-    void* hs;  // H packed into the matrix core's B operands
+    void* hsr;  // H packed for the row side
+    void* hsc;  // H packed for the column side
     float* p1;
     float* p2;
     double* tr_part;
@@ -393,10 +394,10 @@ struct SymLayout {
 };
 size_t sym_layout(void* ws, int64_t n, int k, SymLayout* L) {
     Carve c(ws);
-    const SqPlan pk = sq_plan((int)n, k);
     const SymPlan sp = sym_plan((int)n, k);
     SymLayout l;
-    l.hs = c.take<char>(pk.packed_bytes);
+    l.hsr = c.take<char>(sp.packed_row_bytes);
+    l.hsc = c.take<char>(sp.packed_col_bytes);
     l.p1 = c.take<float>(sp.p1_floats);
     l.p2 = c.take<float>(sp.p2_floats);
     l.tr_part = c.take<double>((size_t)cdiv(n, kUpdRows));
@@ -663,12 +664,11 @@ int symnmf_sh_sym(const float* S, int64_t n, int64_t lds, const float* H, int32_
     SymLayout L;
     sym_layout(ws, n, k, &L);
     hipStream_t st = as_stream(hip_stream);
-    const SqPlan pk = sq_plan((int)n, k);
     const SymPlan sp = sym_plan((int)n, k);
-    HIPCHK(launch_sq_pack(H, k, (int)n, k, pk, L.hs, st));
+    HIPCHK(launch_sym_pack(H, (int)n, k, sp, L.hsr, L.hsc, st));
     {
         ProfScope ps(SYMNMF_PROF_SH_SYM, 2.0 * n * (double)(n + 1) + 8.0 * n * k, st);
-        HIPCHK(launch_sym(S, lds, L.hs, (int)n, k, sp, L.p1, L.p2, st));
+        HIPCHK(launch_sym(S, lds, L.hsr, L.hsc, (int)n, k, sp, L.p1, L.p2, st));
     }
     HIPCHK(launch_sym_fold(L.p1, L.p2, (int)n, k, sp, P, H, L.tr_part, st));
     if (tr_host) {
