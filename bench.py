@@ -5,9 +5,12 @@ One timed step is one whole job on one synthetic returns window resident in
 HBM: build |corr| S (n x n fp32) with the MFMA Gram, run the spectral probe
 (top 64 eigenvalues), fit S ~ H H^T with the AdaptGrow-selected solver to
 convergence, and take the argmax labels. ``value`` is the number of SymNMF
-iterations completed per second of whole-job time. The S.H kernel's achieved
+iterations completed per second of whole-job time. The full-batch steps and
+anchors take S H from the upper triangle of S (``--sh-pass upper``, the
+default for k <= 32; ``rows`` streams all of S). The dominant kernel's achieved
 HBM bandwidth is measured live with HIP events on the launch stream (the
-library's kernel timing) over the timed region.
+library's kernel timing) over the timed region; a full-batch run with the
+row-panel pass is timed beside it for reference.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W]
 """
@@ -35,6 +38,9 @@ def parse():
     ap.add_argument("--warmup", type=int, default=1)
     ap.add_argument("--workload", default="tfactor_n100000_k24")
     ap.add_argument("--solver", default="auto", choices=["auto", "full", "block_svrg"])
+    ap.add_argument("--sh-pass", default="upper", choices=["upper", "rows"],
+                    help="S.H product of the full-batch steps and anchors: the upper-triangle "
+                         "pass (half the bytes of S, k <= 32) or full row panels")
     ap.add_argument("--probe-p", type=int, default=64)
     ap.add_argument("--probe-iters", type=int, default=300)
     ap.add_argument("--max-iters", type=int, default=2000)
@@ -99,12 +105,12 @@ def cpu_baseline(w, k, rows, seconds=10.0):
             "seconds_per_iter": per_iter}
 
 
-def measured_traffic():
-    """HBM bytes per launch of the full S.H pass from the committed rocprofv3
-    counter summary, if the kernel source is the one those counters were taken
-    on (else None)."""
+def measured_traffic(name):
+    """HBM bytes per launch of a kernel from its committed rocprofv3 counter
+    summary, if the kernel source is the one those counters were taken on
+    (else None)."""
     import hashlib
-    path = os.path.join(ROOT, "profiles", "sh_panel_n100000_k24_traffic.json")
+    path = os.path.join(ROOT, "profiles", name)
     try:
         rec = json.load(open(path))
         src = open(os.path.join(ROOT, rec["source"]), "rb").read()
@@ -134,6 +140,8 @@ def main():
     X = torch.from_numpy(w.X).to(dev)
     S = api.alloc_S(n, dev)
 
+    sh_pass = args.sh_pass if k <= 32 else "rows"
+
     def job(kind="abscorr", seed=0):
         ph = {}
         torch.cuda.synchronize()
@@ -149,7 +157,7 @@ def main():
         ph["probe_converged"] = bool(pconv)
         t = time.perf_counter()
         res = api.fit(S, k, solver=args.solver, eigvals=ev, max_iters=args.max_iters,
-                      tol_rel=1e-6, seed=seed)
+                      tol_rel=1e-6, seed=seed, sh_pass=sh_pass)
         torch.cuda.synchronize()
         ph["fit_s"] = time.perf_counter() - t
         t = time.perf_counter()
@@ -188,18 +196,41 @@ def main():
     api.profile_enable(True)
     torch.cuda.synchronize()
     tf = time.perf_counter()
-    full = api.fit(S, k, solver="full", max_iters=args.full_iters, tol_rel=0.0, seed=0)
+    full = api.fit(S, k, solver="full", max_iters=args.full_iters, tol_rel=0.0, seed=0,
+                   sh_pass=sh_pass)
     torch.cuda.synchronize()
     tf = time.perf_counter() - tf
     api.profile_enable(False)
-    prof_full = api.profile_read(_lib.PROF_SH_FULL)
+    prof_fb = {n_: api.profile_read(i) for i, n_ in ((_lib.PROF_SH_FULL, "sh_full"),
+                                                     (_lib.PROF_SH_SYM, "sh_sym"))}
+    # the row-panel pass on the same S, as a reference beside the upper pass
+    api.profile_reset()
+    api.profile_enable(True)
+    torch.cuda.synchronize()
+    tr_ = time.perf_counter()
+    api.fit(S, k, solver="full", max_iters=args.full_iters, tol_rel=0.0, seed=0, sh_pass="rows")
+    torch.cuda.synchronize()
+    tr_ = time.perf_counter() - tr_
+    api.profile_enable(False)
+    prof_rows = api.profile_read(_lib.PROF_SH_FULL)
 
-    sh = prof["sh_full"] if prof["sh_full"]["launches"] else prof_full
-    sh_ms = sh["ms"] / max(1, sh["launches"])
-    sh_bytes = sh["bytes"] / max(1, sh["launches"])
-    achieved = sh_bytes / (sh_ms * 1e-3) / 1e9
+    def rate(d):
+        ms = d["ms"] / max(1, d["launches"])
+        by = d["bytes"] / max(1, d["launches"])
+        return ms, by, by / (ms * 1e-3) / 1e9
+
+    if sh_pass == "upper":
+        dom = prof["sh_sym"] if prof["sh_sym"]["launches"] else prof_fb["sh_sym"]
+        dom_name = "sym_kernel (upper-triangle S.H pass)"
+        traffic_file = "sym_n100000_k24_traffic.json"
+    else:
+        dom = prof["sh_full"] if prof["sh_full"]["launches"] else prof_rows
+        dom_name = "sh_panel_kernel (full S.H pass)"
+        traffic_file = "sh_panel_n100000_k24_traffic.json"
+    sh_ms, sh_bytes, achieved = rate(dom)
+    rows_ms, rows_bytes, rows_gbs = rate(prof_rows)
     kernels = {}
-    for name, d in list(prof.items()) + [("sh_full_fullbatch_run", prof_full)]:
+    for name, d in list(prof.items()) + [("sh_full_rows_reference_run", prof_rows)]:
         if d["launches"]:
             ms = d["ms"] / d["launches"]
             kernels[name] = {"launches": d["launches"], "avg_ms": ms,
@@ -220,12 +251,17 @@ def main():
         "data": "synthetic",
         "config": {"workload": args.workload, "n": n, "k": k, "T": T, "S": "abscorr",
                    "solver": args.solver, "probe_p": args.probe_p, "tol_rel": 1e-6,
-                   "parallelism": "single-gpu"},
+                   "sh_pass": sh_pass, "parallelism": "single-gpu"},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBS,
-                     "traffic": measured_traffic() if args.workload == "tfactor_n100000_k24" else None,
-                     "kernel": "sh_panel_kernel (full S.H pass)", "avg_ms": sh_ms,
-                     "bytes_per_launch": sh_bytes},
+                     "traffic": (measured_traffic(traffic_file)
+                                 if args.workload == "tfactor_n100000_k24" else None),
+                     "kernel": dom_name, "avg_ms": sh_ms, "bytes_per_launch": sh_bytes,
+                     "rows_pass": {"kernel": "sh_panel_kernel", "avg_ms": rows_ms,
+                                   "achieved": rows_gbs, "frac": rows_gbs / HBM_PEAK_GBS,
+                                   "bytes_per_launch": rows_bytes,
+                                   "traffic": (measured_traffic("sh_panel_n100000_k24_traffic.json")
+                                               if args.workload == "tfactor_n100000_k24" else None)}},
         "job": {"fit_iterations": rep["iterations"], "converged": bool(rep["converged"]),
                 "start_branch": "full" if rep["start_branch"] == 0 else "block_svrg",
                 "final_branch": "full" if rep["final_branch"] == 0 else "block_svrg",
@@ -239,7 +275,9 @@ def main():
                 "fit_iters_per_s": rep["iterations"] / float(np.median([p["fit_s"] for p in phases])),
                 "ari_vs_planted": ari, "lambda_top3": [float(x) for x in ev[:3]],
                 "lambda_k_k1_k2": [float(ev[k - 1]), float(ev[k]), float(ev[k + 1])]},
-        "full_batch": {"iters_per_s": args.full_iters / tf, "steps": args.full_iters},
+        "full_batch": {"iters_per_s": args.full_iters / tf, "steps": args.full_iters,
+                       "sh_pass": sh_pass,
+                       "rows_pass_iters_per_s": args.full_iters / tr_},
         "kernels": kernels,
     }
     if args.seeds > 0:

@@ -60,6 +60,14 @@ enum symnmf_kind { SYMNMF_ABSCORR = 0, SYMNMF_TPDM = 1 };
 /* Solvers (P1 "Factorizing with SymNMF", "Why this solver"; P2 sketch). */
 enum symnmf_solver { SYMNMF_AUTO = 0, SYMNMF_FULL = 1, SYMNMF_BLOCK_SVRG = 2 };
 
+/* The S.H product of the fit's full-batch steps and anchor refreshes.
+ * ROWS streams all of S in row panels (symnmf_sh). UPPER reads only the 32 x 32
+ * blocks on or above the diagonal, each serving both of its products
+ * (symnmf_sh_sym; P1 "Factorization at scale", "The problem": S = S^T): half
+ * the bytes of S per step, for k <= 32, with a workspace larger by about
+ * k n^2 / 256 bytes. The Block-SVRG sampled steps read row panels either way. */
+enum symnmf_sh_pass { SYMNMF_SH_ROWS = 0, SYMNMF_SH_UPPER = 1 };
+
 /* Initialisation of H (P1 "Factorizing with SymNMF": the same fixed-seed
  * initialisation for every window; P2 sketch: scale-matched). */
 enum symnmf_init {
@@ -105,6 +113,8 @@ typedef struct symnmf_fit_params {
                               the AdaGrad-family solvers of P3's abstract (Tieleman and
                               Hinton 2012): G = rms_decay G + (1 - rms_decay) g*g; the
                               projected step is unchanged. Applies to every step.      */
+    int32_t sh_pass;       /* enum symnmf_sh_pass: the S.H product of the full-batch
+                              steps and anchors; default ROWS                           */
 } symnmf_fit_params;
 
 typedef struct symnmf_fit_report {

@@ -23,6 +23,7 @@ E_DEGENERATE = -5
 ABSCORR, TPDM = 0, 1
 AUTO, FULL, BLOCK_SVRG = 0, 1, 2
 INIT_UNIFORM, INIT_SCALE_MATCHED, INIT_CALLER = 0, 1, 2
+SH_ROWS, SH_UPPER = 0, 1
 OP_BUILD_S, OP_PROBE, OP_FIT, OP_SH, OP_KMEANS, OP_SQ, OP_SH_SYM = 0, 1, 2, 3, 4, 5, 6
 (PROF_SH_FULL, PROF_SH_SAMPLED, PROF_SH_PROBE, PROF_BUILD_GRAM, PROF_UPDATE,
  PROF_SH_KMEANS, PROF_SH_SYM) = 0, 1, 2, 3, 4, 5, 6
@@ -50,6 +51,7 @@ class FitParams(ctypes.Structure):
         ("check_every", ctypes.c_int32),
         ("resume", ctypes.c_int32),
         ("rms_decay", ctypes.c_double),
+        ("sh_pass", ctypes.c_int32),
     ]
 
 

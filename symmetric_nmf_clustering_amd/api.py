@@ -187,6 +187,8 @@ def fit_params(**kw) -> L.FitParams:
             val = _SOLVERS[val]
         if key == "init" and isinstance(val, str):
             val = _INITS[val]
+        if key == "sh_pass" and isinstance(val, str):
+            val = {"rows": L.SH_ROWS, "upper": L.SH_UPPER}[val]
         if not hasattr(p, key):
             raise TypeError(f"unknown fit parameter {key}")
         setattr(p, key, val)
@@ -200,7 +202,8 @@ def fit(S: torch.Tensor, k: int, *, eigvals=None, H0: Optional[torch.Tensor] = N
 
     ``params`` are the fields of symnmf_fit_params (solver, max_iters, lr, eps,
     block_rows, init, phi0, gap_threshold, tol_rel, stall_tol, init_scale,
-    seed, check_every). H0 sets init='caller'; G0 sets resume=1."""
+    seed, check_every, rms_decay, sh_pass). H0 sets init='caller'; G0 sets
+    resume=1."""
     n, lds = _S_layout(S)
     if H0 is not None:
         params.setdefault("init", L.INIT_CALLER)

@@ -336,12 +336,12 @@ __global__ __launch_bounds__(64 * kSymWaves) void sym_kernel(
             }
 }
 
-// P[i][c] = sum over s >= i / 512 of P1[s][i][c], then over the chunks of
+// P[i][c] (ld ldP) = sum over s >= i / 512 of P1[s][i][c], then over the chunks of
 // strip i / 512 of P2[qc][s(i)][i][c]; tr_part[b] = sum over the rows of block
 // b of <Hdot_i, P_i> (fp64), blocks of kUpdRows rows.
 __global__ __launch_bounds__(256) void sym_fold_kernel(const float* __restrict__ P1,
                                                        const float* __restrict__ P2, int n, int k,
-                                                       int NS, float* __restrict__ P,
+                                                       int NS, float* __restrict__ P, int ldP,
                                                        const float* __restrict__ Hdot,
                                                        double* __restrict__ tr_part) {
     __shared__ double redd[4];
@@ -366,7 +366,7 @@ __global__ __launch_bounds__(256) void sym_fold_kernel(const float* __restrict__
         const int64_t qstride = (int64_t)NS * kSymStrip * k;
         sum += ordered_strided_sum(
             P2 + ((int64_t)si * kSymStrip + (i - si * kSymStrip)) * k + c, nch, qstride);
-        P[(int64_t)i * k + c] = sum;
+        P[(int64_t)i * ldP + c] = sum;
         if (Hdot) acc += (double)Hdot[(int64_t)i * k + c] * (double)sum;
     }
     if (tr_part) {
@@ -424,10 +424,11 @@ hipError_t launch_sym(const float* S, int64_t lds, const void* HsR, const void* 
 }
 
 hipError_t launch_sym_fold(const float* P1, const float* P2, int n, int k, const SymPlan& p,
-                           float* P, const float* Hdot, double* tr_part, hipStream_t st) {
+                           float* P, int ldP, const float* Hdot, double* tr_part,
+                           hipStream_t st) {
     const int nblk = (n + kUpdRows - 1) / kUpdRows;
-    hipLaunchKernelGGL(sym_fold_kernel, dim3(nblk), dim3(256), 0, st, P1, P2, n, k, p.ns, P, Hdot,
-                       tr_part);
+    hipLaunchKernelGGL(sym_fold_kernel, dim3(nblk), dim3(256), 0, st, P1, P2, n, k, p.ns, P, ldP,
+                       Hdot, tr_part);
     return hipGetLastError();
 }
 

@@ -79,8 +79,8 @@ hipError_t launch_sq_split(const float* S, int64_t lds, const void* Qs, int n, i
 // The pass writes row-side partials P1 (one per 512-column strip and row,
 // compact: strip s holds rows [0, min(n, 512 (s + 1)))) and column-side
 // partials P2 (one per 4096-row chunk, strip and column of the strip); the
-// fold adds them in a fixed order into P (n x k, ld k), with the trace
-// partials as launch_reduce_partials.
+// fold adds them in a fixed order into P (n x k, ld ldP), with the trace
+// partials as launch_reduce_partials (Hdot n x k, ld k).
 constexpr int kSymStrip = 512;   // columns per strip
 constexpr int kSymChunk = 4096;  // rows per chunk
 constexpr int kSymMaxK = 32;     // widest factor of the symmetric pass
@@ -100,7 +100,7 @@ hipError_t launch_sym_pack(const float* H, int n, int k, const SymPlan& p, void*
 hipError_t launch_sym(const float* S, int64_t lds, const void* HsR, const void* HsC, int n, int k,
                       const SymPlan& p, float* P1, float* P2, hipStream_t st);
 hipError_t launch_sym_fold(const float* P1, const float* P2, int n, int k, const SymPlan& p,
-                           float* P, const float* Hdot, double* tr_part, hipStream_t st);
+                           float* P, int ldP, const float* Hdot, double* tr_part, hipStream_t st);
 // D[j][c] = H[j][c] - Ha[j][c] (fp32) for the rows j of the nsel listed row
 // blocks of block_rows rows (the Block-SVRG correction's input); other rows
 // of D are left as they are.

@@ -442,10 +442,13 @@ struct FitLayout {
     FitDev* fd;
     double* f_trace;
     float *Hb[2], *Gb[2], *Ha, *Pa, *D, *part, *gram_part;
+    void *sym_hsr, *sym_hsc;  // upper-triangle pass (sh_pass UPPER only)
+    float *sym_p1, *sym_p2;
     double *tr_part, *stats_part, *stats_out;
     int *blocks, *zero_rows;
 };
-size_t fit_layout(void* ws, int64_t n, int k, int max_iters, int block_rows, FitLayout* L) {
+size_t fit_layout(void* ws, int64_t n, int k, int max_iters, int block_rows, int sh_pass,
+                  FitLayout* L) {
     Carve c(ws);
     const int nb = (int)cdiv(n, block_rows);
     const int nblk = (int)cdiv(n, kUpdRows);
@@ -464,6 +467,15 @@ size_t fit_layout(void* ws, int64_t n, int k, int max_iters, int block_rows, Fit
     l.stats_out = c.take<double>(2);
     l.blocks = c.take<int>((size_t)2 * nb + 16);
     l.zero_rows = c.take<int>(1);
+    l.sym_hsr = l.sym_hsc = nullptr;
+    l.sym_p1 = l.sym_p2 = nullptr;
+    if (sh_pass == SYMNMF_SH_UPPER) {
+        const SymPlan sp = sym_plan((int)n, k);
+        l.sym_hsr = c.take<char>(sp.packed_row_bytes);
+        l.sym_hsc = c.take<char>(sp.packed_col_bytes);
+        l.sym_p1 = c.take<float>(sp.p1_floats);
+        l.sym_p2 = c.take<float>(sp.p2_floats);
+    }
     if (L) *L = l;
     return c.off;
 }
@@ -536,6 +548,7 @@ void symnmf_fit_params_default(symnmf_fit_params* p) {
     p->check_every = 16;
     p->resume = 0;
     p->rms_decay = 0.0;
+    p->sh_pass = SYMNMF_SH_ROWS;
 }
 
 size_t symnmf_workspace_bytes(int op, int64_t n, int32_t k_or_p, int64_t T,
@@ -567,7 +580,9 @@ size_t symnmf_workspace_bytes(int op, int64_t n, int32_t k_or_p, int64_t T,
             symnmf_fit_params_default(&d);
             const symnmf_fit_params* p = prm ? prm : &d;
             if (p->max_iters < 0 || p->block_rows < 4) return 0;
-            return fit_layout(nullptr, n, k_or_p, p->max_iters, p->block_rows, nullptr);
+            if (p->sh_pass == SYMNMF_SH_UPPER && k_or_p > kSymMaxK) return 0;
+            return fit_layout(nullptr, n, k_or_p, p->max_iters, p->block_rows, p->sh_pass,
+                              nullptr);
         }
         default: return 0;
     }
@@ -670,7 +685,7 @@ int symnmf_sh_sym(const float* S, int64_t n, int64_t lds, const float* H, int32_
         ProfScope ps(SYMNMF_PROF_SH_SYM, 2.0 * n * (double)(n + 1) + 8.0 * n * k, st);
         HIPCHK(launch_sym(S, lds, L.hsr, L.hsc, (int)n, k, sp, L.p1, L.p2, st));
     }
-    HIPCHK(launch_sym_fold(L.p1, L.p2, (int)n, k, sp, P, H, L.tr_part, st));
+    HIPCHK(launch_sym_fold(L.p1, L.p2, (int)n, k, sp, P, k, H, L.tr_part, st));
     if (tr_host) {
         HIPCHK(launch_sum_doubles(L.tr_part, cdiv(n, kUpdRows), L.tr_out, st));
         HIPCHK(hipMemcpyAsync(tr_host, L.tr_out, sizeof(double), hipMemcpyDeviceToHost, st));
@@ -927,7 +942,8 @@ int symnmf_fit(const float* S, int64_t n, int64_t lds, int32_t k, const symnmf_f
         lds % 4 || !aligned(S, 16) || !aligned(H, 4))
         return SYMNMF_E_INVALID;
     if (P.solver < 0 || P.solver > 2 || P.max_iters < 0 || !(P.eps > 0.0) || P.block_rows < 4 ||
-        !(P.rms_decay >= 0.0 && P.rms_decay < 1.0) ||
+        !(P.rms_decay >= 0.0 && P.rms_decay < 1.0) || P.sh_pass < 0 || P.sh_pass > 1 ||
+        (P.sh_pass == SYMNMF_SH_UPPER && k > kSymMaxK) ||
         !(P.tol_rel >= 0.0) || !(P.stall_tol >= 0.0) || P.init < 0 || P.init > 2 ||
         !(P.gap_threshold > 0.0) || (P.resume && !G) || (obj_trace_cap > 0 && !obj_trace_host) ||
         obj_trace_cap < 0 || !std::isfinite(P.lr) || !std::isfinite(P.phi0))
@@ -936,10 +952,10 @@ int symnmf_fit(const float* S, int64_t n, int64_t lds, int32_t k, const symnmf_f
     const int nb = (int)cdiv(n, P.block_rows);
     const bool need_eig = P.solver != SYMNMF_FULL && !(P.phi0 > 0.0) && nb > 1;
     if (need_eig && (!eigvals_host || n_eig < k + 2)) return SYMNMF_E_INVALID;
-    const size_t need = fit_layout(nullptr, n, k, P.max_iters, P.block_rows, nullptr);
+    const size_t need = fit_layout(nullptr, n, k, P.max_iters, P.block_rows, P.sh_pass, nullptr);
     if (!ws_ok(ws, ws_bytes, need)) return SYMNMF_E_WORKSPACE;
     FitLayout L;
-    fit_layout(ws, n, k, P.max_iters, P.block_rows, &L);
+    fit_layout(ws, n, k, P.max_iters, P.block_rows, P.sh_pass, &L);
     hipStream_t st = as_stream(hip_stream);
     const int nn = (int)n;
     const int64_t nk = (int64_t)n * k;
@@ -1003,26 +1019,41 @@ int symnmf_fit(const float* S, int64_t n, int64_t lds, int32_t k, const symnmf_f
 
     const FullPlan fpl = full_plan(nn);
     const double sh_bytes = 4.0 * n * (double)n + 8.0 * (double)nk;
+    const double sym_bytes = 2.0 * n * (double)(n + 1) + 8.0 * (double)nk;
     int cur = 0, t = 0, doublings = 0, anchors = 0, last_exact = -1;
     double f_anchor_prev = std::nan("");
     bool have_anchor_prev = false;
     FitDev hd;
     std::vector<int> perm, lists;
 
+    const bool upper = P.sh_pass == SYMNMF_SH_UPPER;
+    const SymPlan symp = sym_plan(nn, k);
     auto exact_step = [&](bool write_anchor, int flags) -> int {
-        {
+        if (upper) {
+            // P_t = S H_t from the upper triangle, folded into the first
+            // partial slot (the update then reads one partial)
+            HIPCHK(launch_sym_pack(L.Hb[cur], nn, k, symp, L.sym_hsr, L.sym_hsc, st));
+            {
+                ProfScope ps(SYMNMF_PROF_SH_SYM, sym_bytes, st);
+                HIPCHK(launch_sym(S, lds, L.sym_hsr, L.sym_hsc, nn, k, symp, L.sym_p1, L.sym_p2,
+                                  st));
+            }
+            HIPCHK(launch_sym_fold(L.sym_p1, L.sym_p2, nn, k, symp, L.part, ldp, nullptr, nullptr,
+                                   st));
+        } else {
             ProfScope ps(SYMNMF_PROF_SH_FULL, sh_bytes, st);
             HIPCHK(launch_sh_panel(S, lds, L.Hb[cur], k, fpl.rp, fpl.nsplit, L.part, ldp, st));
         }
+        const int nsplit = upper ? 1 : fpl.nsplit;
         UpdateArgs a{};
-        a.n = nn; a.k = k; a.ldp = ldp; a.part = L.part; a.nsplit = fpl.nsplit;
+        a.n = nn; a.k = k; a.ldp = ldp; a.part = L.part; a.nsplit = nsplit;
         a.pstride = (int64_t)n * ldp; a.H = L.Hb[cur]; a.G = L.Gb[cur];
         a.Hn = L.Hb[cur ^ 1]; a.Gn = L.Gb[cur ^ 1];
         a.Ha = write_anchor ? L.Ha : nullptr; a.Pa = write_anchor ? L.Pa : nullptr;
         a.fd = L.fd; a.lr = (float)lr; a.eps = (float)P.eps; a.decay = (float)P.rms_decay;
         a.tr_part = L.tr_part; a.gram_part = L.gram_part;
         {
-            ProfScope ps(SYMNMF_PROF_UPDATE, (double)nk * 4.0 * (5 + fpl.nsplit), st);
+            ProfScope ps(SYMNMF_PROF_UPDATE, (double)nk * 4.0 * (5 + nsplit), st);
             HIPCHK(launch_update(a, st));
         }
         HIPCHK(launch_finalize(L.fd, L.f_trace, t, nblk, k, L.tr_part, L.gram_part, flags, st));

@@ -7,7 +7,8 @@ the probe's product ``symnmf_sq`` on a signed n x k basis instead) and a plain
 element-wise kernel that reads ``--copy-mib`` MiB and writes as many. Under
 ``rocprofv3 --pmc FETCH_SIZE`` (or ``WRITE_SIZE``) that kernel's per-dispatch
 counter value gives the factor that turns the counter into bytes; the S.H dispatches then give the
-HBM traffic of one pass. Prints one JSON line with HIP-event timings.
+HBM traffic of one pass. ``--op sym`` runs the upper-triangle pass (``symnmf_sh_sym``)
+instead. Prints one JSON line with HIP-event timings.
 
 Usage: python -m symmetric_nmf_clustering_amd.profile_passes [--n 100000] [--k 24]
 
@@ -15,7 +16,8 @@ Usage: python -m symmetric_nmf_clustering_amd.profile_passes [--n 100000] [--k 2
 (no GPU needed):
 
     python -m symmetric_nmf_clustering_amd.profile_passes summarize \
-        --fetch-csv F.csv --fetch-json F.json --write-csv W.csv --write-json W.json --out OUT.json
+        --fetch-csv F.csv --fetch-json F.json --write-csv W.csv --write-json W.json --out OUT.json \
+        [--op sh|sym]
 
 where F/W are rocprofv3's ``*_counter_collection.csv`` of the FETCH_SIZE and
 WRITE_SIZE runs and the JSON files hold this module's printed line of each run.
@@ -33,6 +35,13 @@ import sys
 COPY_REPS = 3
 # the full S.H pass: contiguous row splits (row mode 0)
 FULL_PASS = re.compile(r"sh_panel_kernel<(\d+), (\d+), (\d+), (true|false), 0>")
+# the upper-triangle pass
+SYM_PASS = re.compile(r"sym_kernel<(\d+)>")
+KERNELS = {
+    # op: (dispatch name pattern, source file, algorithmic bytes per launch)
+    "sh": (FULL_PASS, "k_sh.hip", lambda n, k: 4.0 * n * n + 8.0 * n * k),
+    "sym": (SYM_PASS, "k_sym.hip", lambda n, k: 2.0 * n * (n + 1) + 8.0 * n * k),
+}
 CALIBRATION = "MulFunctor"
 
 
@@ -53,17 +62,19 @@ def summarize(argv):
     ap.add_argument("--write-csv", required=True)
     ap.add_argument("--write-json", required=True)
     ap.add_argument("--out", required=True)
+    ap.add_argument("--op", choices=sorted(KERNELS), default="sh")
     args = ap.parse_args(argv)
+    pattern, src_name, algo_bytes = KERNELS[args.op]
     rec = {}
     for counter, cpath, jpath in (("FETCH_SIZE", args.fetch_csv, args.fetch_json),
                                   ("WRITE_SIZE", args.write_csv, args.write_json)):
         rows = _counter_rows(cpath, counter)
         run = _last_json(jpath)
-        sh = [r for r in rows if FULL_PASS.search(r["Kernel_Name"])]
+        sh = [r for r in rows if pattern.search(r["Kernel_Name"])]
         cal = [r for r in rows if CALIBRATION in r["Kernel_Name"]]
         if not sh or not cal:
-            raise SystemExit(f"{cpath}: no full-pass or calibration dispatches")
-        names = {FULL_PASS.search(r["Kernel_Name"]).group(0) for r in sh}
+            raise SystemExit(f"{cpath}: no {args.op} or calibration dispatches")
+        names = {pattern.search(r["Kernel_Name"]).group(0) for r in sh}
         if len(names) != 1:
             raise SystemExit(f"{cpath}: several full-pass kernels {sorted(names)}")
         cal_bytes = run["copy_bytes_each_way"] * run["copy_reps"]
@@ -81,8 +92,8 @@ def summarize(argv):
     rec["traffic_bytes_per_launch"] = (rec["fetch_size_kib_per_launch"] * 1024.0 * rec["fetch_size_factor"]
                                        + rec["write_size_kib_per_launch"] * 1024.0 * rec["write_size_factor"])
     n, k = rec["n"], rec["k"]
-    rec["algorithmic_bytes_per_launch"] = 4.0 * n * n + 8.0 * n * k
-    src = os.path.join("symmetric_nmf_clustering_amd", "csrc", "k_sh.hip")
+    rec["algorithmic_bytes_per_launch"] = algo_bytes(n, k)
+    src = os.path.join("symmetric_nmf_clustering_amd", "csrc", src_name)
     root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
     rec["source"] = src
     rec["source_sha256"] = hashlib.sha256(open(os.path.join(root, src), "rb").read()).hexdigest()
@@ -102,7 +113,7 @@ def main(argv=None):
     ap.add_argument("--T", type=int, default=252)
     ap.add_argument("--passes", type=int, default=4)
     ap.add_argument("--copy-mib", type=int, default=4096)
-    ap.add_argument("--op", choices=("sh", "sq"), default="sh")
+    ap.add_argument("--op", choices=("sh", "sq", "sym"), default="sh")
     args = ap.parse_args(argv)
 
     import numpy as np
@@ -115,7 +126,7 @@ def main(argv=None):
                              min_size=min(64, args.n // args.k))
     X = torch.from_numpy(w.X).cuda()
     S, _ = api.build_S(X, "abscorr")
-    if args.op == "sh":
+    if args.op in ("sh", "sym"):
         H = torch.from_numpy(synth.random_factor(args.n, args.k, seed=0, scale=0.1)).cuda()
     else:
         rng = np.random.default_rng(0)
@@ -126,11 +137,14 @@ def main(argv=None):
     for _ in range(args.passes):
         if args.op == "sh":
             api.sh(S, H)
+        elif args.op == "sym":
+            api.sh_sym(S, H)
         else:
             api.sq(S, H)
     torch.cuda.synchronize()
     api.profile_enable(False)
-    sh = api.profile_read(_lib.PROF_SH_FULL if args.op == "sh" else _lib.PROF_SH_PROBE)
+    sh = api.profile_read({"sh": _lib.PROF_SH_FULL, "sym": _lib.PROF_SH_SYM,
+                           "sq": _lib.PROF_SH_PROBE}[args.op])
     # calibration: an element-wise kernel that reads copy_mib MiB and writes
     # copy_mib MiB (a contiguous copy_() would go to a DMA engine instead)
     nfl = args.copy_mib * (1 << 20) // 4

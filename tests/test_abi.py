@@ -110,6 +110,14 @@ def test_workspace_is_order_nk(golden_dir):
     assert lib.symnmf_workspace_bytes(L.OP_PROBE, n, 113, 0, None) == 0  # w > 128
     assert lib.symnmf_workspace_bytes(L.OP_SQ, n, 129, 0, None) == 0     # w > 128
     assert lib.symnmf_workspace_bytes(L.OP_SH_SYM, n, 33, 0, None) == 0  # k > 32
+    up = L.FitParams()
+    lib.symnmf_fit_params_default(ctypes.byref(up))
+    up.sh_pass = L.SH_UPPER
+    base = lib.symnmf_workspace_bytes(L.OP_FIT, n, k, 0, None)
+    with_sym = lib.symnmf_workspace_bytes(L.OP_FIT, n, k, 0, ctypes.byref(up))
+    # the upper-triangle pass adds its partials (~k n^2 / 256 bytes) on request only
+    assert base < with_sym < base + 4.0 * n * n * k / 1024 * 1.3 + 40 * n * k * 4
+    assert lib.symnmf_workspace_bytes(L.OP_FIT, n, 33, 0, ctypes.byref(up)) == 0
     # the packed Q (6 bytes per element, 32-row blocks, 16-column tiles) and partials
     assert lib.symnmf_workspace_bytes(L.OP_SQ, n, 80, 0, None) >= 6 * n * 80
     assert lib.symnmf_workspace_bytes(L.OP_BUILD_S, n, 1, 1, None) == 0  # T < 2
@@ -192,6 +200,8 @@ def test_fit_argument_validation():
     assert call(P(max_iters=-1, **full)) == L.E_INVALID
     assert call(P(resume=1, **full)) == L.E_INVALID                 # resume needs G
     assert call(P(init=L.INIT_UNIFORM, init_scale=0.0, **full)) == L.E_INVALID
+    assert call(P(sh_pass=2, **full)) == L.E_INVALID
+    assert call(P(sh_pass=L.SH_UPPER, **full), n=100, lds=100, k=33) == L.E_INVALID   # k > 32
     assert call(P(solver=9)) == L.E_INVALID
     # AUTO with several blocks needs eigenvalues (>= k + 2) unless phi0 > 0
     assert call(P(block_rows=10)) == L.E_INVALID

@@ -130,3 +130,76 @@ def test_sh_sym_rejects_wide_factor(torch, api):
     Sd = S_to_dev(synth.random_symmetric_nonneg(n, seed=1), torch)
     with pytest.raises(ValueError):
         api.sh_sym(Sd, to_dev(np.zeros((n, 33)), torch))
+
+
+# ---- the fit with the upper-triangle pass (sh_pass='upper') -----------------
+
+def _traj_rel(fg, fr, s2):
+    fg, fr = np.asarray(fg, np.float64), np.asarray(fr, np.float64)
+    return np.abs(fg - fr) / np.maximum(np.abs(fr), 1e-12 * s2)
+
+
+def _labels_agree(Hg, Hr):
+    from sklearn.metrics import adjusted_rand_score
+    return adjusted_rand_score(np.asarray(Hg).argmax(axis=1), np.asarray(Hr).argmax(axis=1))
+
+
+def test_fit_upper_c1_trajectory(torch, api):
+    """n=1024, k=8, H0 ~ U(0, 0.1), lr 0.05, 200 full-batch steps, every S H
+    from the upper triangle: the oracle's fp64 trajectory to 1e-3 of ||S||^2."""
+    w = synth.workload("blocks_n1024_k8")
+    S = oracle.abs_corr(w.X).astype(np.float32)
+    res = api.fit(S_to_dev(S, torch), w.k, solver="full", init="uniform", init_scale=0.1, seed=0,
+                  lr=0.05, max_iters=200, tol_rel=0.0, sh_pass="upper")
+    ref = oracle.fit_full(S, oracle.init_uniform(w.n, w.k, 0.1, 0), 0.05, 200, tol=0.0)
+    s2 = float((S.astype(np.float64) ** 2).sum())
+    assert res.report["iterations"] == 200
+    assert _traj_rel(res.f_trace, ref["f"], s2).max() <= 1e-3
+    assert _labels_agree(res.H.cpu().numpy(), ref["H"]) >= 0.99
+
+
+def test_fit_upper_block_svrg_c3(torch, api):
+    """n=8192, k=24 TPDM, Block-SVRG from 1 of 8 blocks: the anchors' exact
+    products and the full-batch tail from the upper triangle, the sampled
+    steps from row panels; same anchors, doublings and trajectory as the
+    oracle's AdaptGrow."""
+    w = synth.workload("tstress_n8192_k24")
+    S = oracle.tpdm(w.X, 0.05).astype(np.float32)
+    S64 = S.astype(np.float64)
+    iters = 240
+    res = api.fit(S_to_dev(S, torch), w.k, solver="block_svrg", phi0=1.0 / 8, block_rows=1024,
+                  max_iters=iters, tol_rel=1e-6, seed=1, sh_pass="upper")
+    m = S64.mean()
+    H0 = oracle.init_uniform(w.n, w.k, oracle.init_scale_matched(m, w.k), 1)
+    ref = oracle.fit_adaptgrow(S64, H0, oracle.default_lr(m, w.k), iters,
+                               solver=oracle.SOLVER_BLOCK_SVRG, phi0=1.0 / 8, block_rows=1024,
+                               tol=1e-6, seed=1)
+    rep = res.report
+    assert rep["iterations"] == ref["iters"]
+    assert rep["doublings"] == len(ref["history"])
+    fg, fr = np.asarray(res.f_trace), np.asarray(ref["f"])
+    assert np.array_equal(np.isnan(fg), np.isnan(fr))
+    ex = ~np.isnan(fr)
+    assert _traj_rel(fg[ex], fr[ex], float((S64 ** 2).sum())).max() <= 1e-3
+    assert _labels_agree(res.H.cpu().numpy(), ref["H"]) >= 0.99
+
+
+def test_fit_upper_agrees_with_rows_and_is_deterministic(torch, api):
+    """The two products differ only in rounding, which the iteration carries
+    along: over 300 full-batch steps the trajectories stay within the bound both
+    keep to the oracle's (1e-3) and the labels agree; two upper runs are
+    identical."""
+    w = synth.workload("blocks_n1024_k8")
+    S = oracle.abs_corr(w.X).astype(np.float32)
+    Sd = S_to_dev(S, torch)
+    kw = dict(solver="full", init="uniform", init_scale=0.1, seed=2, lr=0.05, max_iters=300,
+              tol_rel=0.0)
+    rows = api.fit(Sd, w.k, **kw)
+    up1 = api.fit(Sd, w.k, sh_pass="upper", **kw)
+    up2 = api.fit(Sd, w.k, sh_pass="upper", **kw)
+    assert torch.equal(up1.H, up2.H)
+    s2 = float((S.astype(np.float64) ** 2).sum())
+    assert _traj_rel(up1.f_trace, rows.f_trace, s2).max() <= 1e-3
+    assert _labels_agree(up1.H.cpu().numpy(), rows.H.cpu().numpy()) >= 0.99
+    with pytest.raises(Exception):
+        api.fit(Sd, 33, solver="full", max_iters=1, sh_pass="upper")   # k > 32
