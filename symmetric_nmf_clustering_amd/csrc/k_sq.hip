@@ -63,9 +63,10 @@ __global__ __launch_bounds__(256) void sq_pack_q_kernel(const float* __restrict_
 // the 16 kSqWaveTiles rows from tile * kSqTileRows + 32 w; K blocks
 // [split * kb_per_split, +kb_per_split). The K block's packed Q (NT * 3 KiB)
 // is staged in LDS, double-buffered, one barrier per block; each wave's S rows
-// go straight to registers, two blocks ahead of the multiply.
+// go straight to registers, one block ahead of the multiply.
 template <int NT>
-__global__ __launch_bounds__(256) void sq_split_kernel(const float* __restrict__ S, int64_t lds,
+// Three workgroups per CU (three waves per SIMD: 164 registers, 48 KiB of LDS).
+__global__ __launch_bounds__(256, 3) void sq_split_kernel(const float* __restrict__ S, int64_t lds,
                                                        const u32x4* __restrict__ Qs, int n,
                                                        int kb_per_split, float* __restrict__ part,
                                                        int ldp, int width) {
@@ -143,9 +144,9 @@ __global__ __launch_bounds__(256) void sq_split_kernel(const float* __restrict__
 #pragma unroll
         for (int t = 0; t < NT; ++t) acc[s][t] = floatx4{0.f, 0.f, 0.f, 0.f};
 
-    // One K block: the S values of block kb were loaded two blocks earlier;
-    // this step issues block kb + 1's packed Q and block kb + 2's S values,
-    // multiplies, then stages Q (its wait does not cover the later S loads,
+    // One K block: the S values of block kb were loaded one block earlier;
+    // this step issues block kb + 1's packed Q and S values, multiplies, then
+    // stages Q (its wait does not cover the later S loads,
     // which stay in flight across the barrier). Every step issues its loads,
     // past the split's end of a clamped (valid) block, so that every path
     // holds the same loads and the compiler's wait counts stay tight; only
@@ -153,7 +154,7 @@ __global__ __launch_bounds__(256) void sq_split_kernel(const float* __restrict__
     int buf = 0;
     auto step = [&](int kb, float (&cur)[WM][8], float (&pre)[WM][8]) {
         load_q(min(kb + 1, kb1 - 1));
-        load_a(min(kb + 2, kb1 - 1), pre);
+        load_a(min(kb + 1, kb1 - 1), pre);
         if (kb < kb1) {
             mask_tail(kb, cur);
             u32x4 a1[WM], a2[WM], a3[WM];
@@ -175,17 +176,17 @@ __global__ __launch_bounds__(256) void sq_split_kernel(const float* __restrict__
         buf ^= 1;
     };
 
-    float a0[WM][8], a1[WM][8], a2[WM][8];
+    float a0[WM][8], a1[WM][8];
     load_q(kb0);
     load_a(kb0, a0);
-    load_a(min(kb0 + 1, kb1 - 1), a1);
     store_q(0);
     __syncthreads();
-    // three register sets in rotation, unrolled so that none is copied
-    for (int kb = kb0; kb < kb1; kb += 3) {
-        step(kb, a0, a2);
+    // two register sets in rotation, unrolled so that none is copied (one set
+    // fewer than two blocks ahead would need leaves room for a third wave per
+    // SIMD, which hides more of the matrix-core and LDS latency)
+    for (int kb = kb0; kb < kb1; kb += 2) {
+        step(kb, a0, a1);
         step(kb + 1, a1, a0);
-        step(kb + 2, a2, a1);
     }
 
     // lane l holds rows 4 g + r of each subtile, column 16 t + l % 16
