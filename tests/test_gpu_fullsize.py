@@ -209,11 +209,35 @@ def test_fullsize_tpdm_rows_trace_and_spectrum(big):
         torch.cuda.empty_cache()
 
 
-def test_fullsize_first_step_and_objective(big):
+def test_fullsize_sh_sym_rows(big):
+    """The upper-triangle pass as the benchmark's fit runs it (k = 24, 512-column
+    strips, 4096-row chunks): sampled rows, strip and chunk edges among them,
+    against the oracle's rows built from the returns; the trace against the sum
+    of its own outputs; and the row-panel pass on the same rows."""
+    torch, api, w, S, fro, rows = big
+    rows = np.unique(np.concatenate([rows, [4096, 8191, 8192, 99839, 99840]]))
+    H = synth.random_factor(N, K, seed=3, scale=0.1)
+    Hd = to_dev(H, torch)
+    P, tr = api.sh_sym(S, Hd)
+    Pg = P.cpu().numpy().astype(np.float64)
+    S_rows = oracle.abs_corr_rows(w.X, rows)
+    Pr, _ = oracle.sh_product(S_rows, H, rows=rows)
+    rel = np.abs(Pg[rows] - Pr) / np.abs(Pr)  # S, H >= 0: |P| = |S||H|
+    print(f"upper-triangle pass: max rel error over {rows.size} rows = {rel.max():.2e}")
+    assert rel.max() <= 1e-4, rel.max()
+    assert abs(tr - float((H.astype(np.float64) * Pg).sum())) <= 1e-9 * abs(tr)
+    Pf, trf = api.sh(S, Hd)
+    d = np.abs(Pg[rows] - Pf.cpu().numpy()[rows]) / np.abs(Pr)
+    assert d.max() <= 1e-4, d.max()
+    assert abs(tr - trf) <= 1e-5 * abs(trf)
+
+
+@pytest.mark.parametrize("sh_pass", ["rows", "upper"])
+def test_fullsize_first_step_and_objective(big, sh_pass):
     torch, api, w, S, fro, rows = big
     lr = 0.05
     res = api.fit(S, K, solver="full", init="uniform", init_scale=0.1, seed=5, lr=lr,
-                  max_iters=1, tol_rel=0.0)
+                  max_iters=1, tol_rel=0.0, sh_pass=sh_pass)
     H0 = oracle.init_uniform(N, K, 0.1, 5)
     K0 = H0.T @ H0
     S_rows = oracle.abs_corr_rows(w.X, rows)
@@ -228,7 +252,7 @@ def test_fullsize_first_step_and_objective(big):
     assert np.abs(H1 - H1_ref)[decided].max() <= 1e-5
     # f_0 by the trace identity equals ||S||^2 - 2 tr + ||K0||^2 with the
     # build's ||S||^2 and the S.H pass's trace
-    _, tr0 = api.sh(S, to_dev(H0, torch))
+    _, tr0 = (api.sh if sh_pass == "rows" else api.sh_sym)(S, to_dev(H0, torch))
     f0 = fro - 2.0 * tr0 + float((K0 * K0).sum())
     assert abs(res.f_trace[0] - f0) <= 1e-6 * f0
     assert abs(res.report["S_fro2"] - fro) <= 1e-9 * fro
