@@ -203,3 +203,18 @@ def test_fit_upper_agrees_with_rows_and_is_deterministic(torch, api):
     assert _labels_agree(up1.H.cpu().numpy(), rows.H.cpu().numpy()) >= 0.99
     with pytest.raises(Exception):
         api.fit(Sd, 33, solver="full", max_iters=1, sh_pass="upper")   # k > 32
+
+
+@pytest.mark.parametrize("k", [5, 17])
+def test_fit_upper_odd_width(torch, api, k):
+    """k not a multiple of 4 (the partial products' row pitch is rounded up to
+    4): 60 full-batch steps with the upper-triangle product against the
+    oracle's trajectory on a ragged n."""
+    n = 1003
+    S = synth.random_symmetric_nonneg(n, seed=k).astype(np.float32) / n
+    res = api.fit(S_to_dev(S, torch), k, solver="full", init="uniform", init_scale=0.1, seed=k,
+                  lr=0.02, max_iters=60, tol_rel=0.0, sh_pass="upper")
+    ref = oracle.fit_full(S.astype(np.float64), oracle.init_uniform(n, k, 0.1, k), 0.02, 60, tol=0.0)
+    s2 = float((S.astype(np.float64) ** 2).sum())
+    assert _traj_rel(res.f_trace, ref["f"], s2).max() <= 1e-3
+    assert np.abs(res.H.cpu().numpy() - ref["H"]).max() <= 1e-3 * np.abs(ref["H"]).max()
