@@ -23,8 +23,12 @@ that nothing outside this file can pin say "parity unpinned" below:
 
 * ``tpdm`` constants (loss sign, F = R/(T+1), the 5% tail, 1/m scaling):
   parity unpinned for the constants; the structure is pinned by invariants.
-* ``fit_adaptgrow`` stagnation rule and phi seeding: parity unpinned (the
-  pages name ``stagnating()`` and the seeding but do not define them).
+* ``fit_adaptgrow`` stagnation rule and phi seeding, and the constants of the
+  stopping test (``converged_test``: the 1e-3 stall fraction, the 0.05 floor
+  of the objective scale): parity unpinned for the constants (the pages name
+  ``stagnating()``, the seeding and convergence but define none of them). The
+  schedule these rules drive (anchor steps, doublings, the switch to full
+  batch, the stop step, resumption) is pinned by hand-composed runs.
 * ``calm_windows`` (which windows calibrate the 3-sigma limit) and the
   warm start of ``rolling_fit``: readings of the pages, parity unpinned.
 """
@@ -38,7 +42,7 @@ __all__ = [
     "standardize", "abs_corr", "abs_corr_rows", "tpdm_angles", "tpdm",
     "tpdm_rows", "splitmix64", "uniform24", "init_uniform", "init_scale_matched",
     "default_lr", "sh_product", "objective_explicit", "objective_trace", "gradient",
-    "adagrad_step", "rmsprop_step", "fit_full", "sample_blocks", "svrg_sh_estimate",
+    "adagrad_step", "rmsprop_step", "converged_test", "fit_full", "sample_blocks", "svrg_sh_estimate",
     "gap_ratio", "initial_blocks", "fit_adaptgrow", "top_eigenvalues",
     "subspace_top_eigenvalues",
     "ari_drift", "calm_windows", "control_limit", "cross_block_means", "rolling_fit",
@@ -195,10 +199,18 @@ def sh_product(S, H, rows=None):
     return P, float((Hr * P).sum())
 
 
-def objective_explicit(S, H):
-    """f(H) = ||S - H H^T||_F^2, the plain definition (forms n x n)."""
-    R = np.asarray(S, dtype=np.float64) - H @ H.T
-    return float((R * R).sum())
+def objective_explicit(S, H, rows_per_slice=1024):
+    """f(H) = ||S - H H^T||_F^2, the plain definition: the residual is formed
+    entry by entry, a slice of rows at a time (so that n = 8192 needs no
+    0.5 GB temporary), and its squares summed."""
+    S = np.asarray(S, dtype=np.float64)
+    H = np.asarray(H, dtype=np.float64)
+    n = S.shape[0]
+    f = 0.0
+    for r0 in range(0, n, rows_per_slice):
+        R = S[r0:r0 + rows_per_slice] - H[r0:r0 + rows_per_slice] @ H.T
+        f += float((R * R).sum())
+    return f
 
 
 def objective_trace(S_fro2, H, P):
@@ -239,12 +251,31 @@ def _step(H, G, g, lr, eps, rho):
 # --------------------------------------------------------------------------
 
 
-def fit_full(S, H0, lr, max_iters, tol=0.0, eps=1e-8, G0=None, objective="trace", rho=0.0):
+def converged_test(f_prev, f, tol, steps, floor_abs):
+    """The stopping test (config 2: relative objective change below tol).
+
+    True when |f_prev - f| < tol * steps * max(|f_prev|, floor_abs): the
+    average change per step over ``steps`` steps (1 in the full branch, the
+    epoch length between two Block-SVRG anchors) relative to the objective.
+    Reading: the relative change is ill-posed when the attainable objective is
+    near zero (a TPDM has rank at most m, the number of extreme days, below
+    k, and is factored almost exactly, while AdaGrad's f decays as a power
+    law), so the denominator never falls below ``floor_abs`` =
+    obj_floor * ||S||^2 (obj_floor 0.05: below the 7-10% of ||S||^2 that the
+    |corr| fits keep at convergence, so their test is the plain relative one).
+    """
+    return abs(f_prev - f) < tol * steps * max(abs(f_prev), floor_abs)
+
+
+def fit_full(S, H0, lr, max_iters, tol=0.0, eps=1e-8, G0=None, objective="trace", rho=0.0,
+             obj_floor=0.05):
     """Full-batch projected AdaGrad (RMSprop's accumulator when rho > 0).
 
     Iteration t: P = S H_t; f_t = f(H_t) (before the update); if t >= 1 and
-    |f_{t-1} - f_t| < tol * |f_{t-1}|, stop and return H_t; otherwise take the
-    AdaGrad step. At most ``max_iters`` steps.
+    ``converged_test(f_{t-1}, f_t, tol, 1, obj_floor ||S||^2)``, stop and
+    return H_t; otherwise take the AdaGrad step. At most ``max_iters`` steps.
+    ``objective`` "explicit" evaluates f as ||S - H H^T||^2 directly, "trace"
+    by the identity ||S||^2 - 2 tr(H^T P) + ||H^T H||^2.
     Returns dict(H, G, f (list of f_t), iters (steps taken), converged).
     """
     S = np.asarray(S, dtype=np.float64)
@@ -258,7 +289,7 @@ def fit_full(S, H0, lr, max_iters, tol=0.0, eps=1e-8, G0=None, objective="trace"
         P = S @ H
         f = objective_trace(s2, H, P) if objective == "trace" else objective_explicit(S, H)
         fs.append(f)
-        if tol > 0 and t >= 1 and abs(fs[-2] - f) < tol * abs(fs[-2]):
+        if tol > 0 and t >= 1 and converged_test(fs[-2], f, tol, 1, obj_floor * s2):
             converged = True
             break
         g = 4.0 * (H @ (H.T @ H) - P)
@@ -326,89 +357,120 @@ def initial_blocks(gamma, nb, threshold=5.0):
 
 def fit_adaptgrow(S, H0, lr, max_iters, *, solver=SOLVER_AUTO, eigvals=None, k=None,
                   phi0=0.0, block_rows=1024, gap_threshold=5.0, tol=1e-6,
-                  stall_tol=1e-3, eps=1e-8, seed=0, rho=0.0):
+                  stall_tol=1e-3, obj_floor=0.05, eps=1e-8, seed=0, rho=0.0,
+                  objective="trace", G0=None, state=None):
     """AdaptGrow: full-batch AdaGrad or Block-SVRG with sample growth.
 
     Branch choice: FULL -> full; otherwise |B|0 from phi0 > 0
     (ceil(phi0 nb) clamped to [1, nb]) or from gamma_{k+1} (``initial_blocks``);
     |B|0 = nb means full.
-    Sampled branch (reading; the stagnation rule is parity unpinned): epochs of
-    E = ceil(nb/|B|) steps. The first step of an epoch is an anchor: P = S H
-    exactly, f exact; if a previous anchor exists and
-    (f~prev - f) < stall_tol f~prev the sample doubles (capped at nb; at nb the
-    run continues as full batch, keeping G); the anchor becomes H~ = H,
-    P~ = P and the step uses the exact gradient. Other steps draw
-    ``sample_blocks(seed, t, nb, |B|)`` and use ``svrg_sh_estimate``.
-    f of a sampled step is not computed (NaN in the trace). The full branch
-    tests convergence as ``fit_full`` does, against the previous step's exact f.
+
+    Sampled branch (reading; the stall and stop constants are parity
+    unpinned): with E = ceil(nb/|B|), a step is an anchor when no anchor exists
+    yet or E steps have passed since the last one. An anchor computes P = S H
+    and f exactly, then, against the previous anchor (E_j steps earlier):
+      * stop: ``converged_test(f~prev, f, tol, E_j, obj_floor ||S||^2)`` ends
+        the run and returns this H (the anchor's update is not taken);
+      * stall: (f~prev - f) < stall_tol f~prev doubles |B| (capped at nb; at
+        nb the run continues as full batch, keeping G);
+    and becomes H~ = H, P~ = P; the anchor's own step uses the exact gradient.
+    Other steps draw ``sample_blocks(seed, t, nb, |B|)`` with the absolute step
+    index t and use ``svrg_sh_estimate``; their f is not computed (NaN in the
+    trace). The full branch tests convergence as ``fit_full`` does, against the
+    previous step's exact f (an anchor's f counts).
+
+    Resumption: ``state`` (from a previous call's result) restores the step
+    index, |B|, the anchor (H~, P~, its step and f) and the previous exact f,
+    and ``G0`` the accumulator, so that the two calls take the same steps as one
+    uninterrupted call. ``max_iters`` counts the steps of this call.
+    Returns dict(H, G, f (this call's f_t), iters (steps taken in this call),
+    converged, history [(t, |B|) at each doubling, absolute t], gamma,
+    start_branch, final_branch, nsel, anchors (absolute steps), state).
     """
     S = np.asarray(S, dtype=np.float64)
     H = np.array(H0, dtype=np.float64)
     n, kk = H.shape
     if k is None:
         k = kk
-    G = np.zeros_like(H)
+    G = np.zeros_like(H) if G0 is None else np.array(G0, dtype=np.float64)
     s2 = float(np.einsum("ij,ij->", S, S))  # ||S||_F^2 without an n x n temporary
+    floor_abs = obj_floor * s2
     nb = -(-n // block_rows)
     gamma = None
-    if solver == SOLVER_FULL:
-        nsel = nb
-    elif phi0 > 0:
-        nsel = min(nb, max(1, int(math.ceil(phi0 * nb - 1e-12))))
+    if state is not None:
+        t = int(state["t"])
+        nsel = int(state["nsel"])
+        anchor_t = state["anchor_t"]
+        f_anchor = state["f_anchor"]
+        H_a = None if state["H_a"] is None else np.array(state["H_a"], dtype=np.float64)
+        P_a = None if state["P_a"] is None else np.array(state["P_a"], dtype=np.float64)
+        prev_exact = state["f_prev"]
     else:
-        if eigvals is None:
-            raise ValueError("AdaptGrow needs eigenvalues or phi0")
-        gamma = gap_ratio(eigvals, k)
-        nsel = initial_blocks(gamma, nb, gap_threshold)
+        t = 0
+        if solver == SOLVER_FULL:
+            nsel = nb
+        elif phi0 > 0:
+            nsel = min(nb, max(1, int(math.ceil(phi0 * nb - 1e-12))))
+        else:
+            if eigvals is None:
+                raise ValueError("AdaptGrow needs eigenvalues or phi0")
+            gamma = gap_ratio(eigvals, k)
+            nsel = initial_blocks(gamma, nb, gap_threshold)
+        anchor_t = f_anchor = H_a = P_a = prev_exact = None
     full = nsel >= nb
     start_branch = "full" if full else "sampled"
+
+    def f_of(P):
+        if objective == "trace":
+            K = H.T @ H
+            return float(s2 - 2.0 * (H * P).sum() + (K * K).sum())
+        return objective_explicit(S, H)
+
     fs = []
     history = []
+    anchors = []
     converged = False
-    prev_exact = None  # f of the immediately preceding step, if exact
-    epoch_pos = 0
-    E = -(-nb // nsel)
-    f_anchor_prev = None
-    H_a = P_a = None
-    t = 0
-    while t < max_iters:
-        K = H.T @ H
+    t0 = t
+    while t < t0 + max_iters:
+        E = -(-nb // nsel)
         if full:
             P = S @ H
-            f = float(s2 - 2.0 * (H * P).sum() + (K * K).sum())
+            f = f_of(P)
             fs.append(f)
-            if tol > 0 and prev_exact is not None and abs(prev_exact - f) < tol * abs(prev_exact):
+            if tol > 0 and prev_exact is not None and converged_test(prev_exact, f, tol, 1, floor_abs):
                 converged = True
                 break
             prev_exact = f
-        elif epoch_pos == 0:
+        elif anchor_t is None or t - anchor_t >= E:
             P = S @ H
-            f = float(s2 - 2.0 * (H * P).sum() + (K * K).sum())
+            f = f_of(P)
             fs.append(f)
-            if f_anchor_prev is not None and (f_anchor_prev - f) < stall_tol * f_anchor_prev:
-                nsel = min(2 * nsel, nb)
-                E = -(-nb // nsel)
-                history.append((t, nsel))
-                if nsel >= nb:
-                    full = True
-            prev_exact = f
-            f_anchor_prev = f
+            if anchor_t is not None:
+                if tol > 0 and converged_test(f_anchor, f, tol, t - anchor_t, floor_abs):
+                    converged = True
+                    break
+                if (f_anchor - f) < stall_tol * f_anchor:
+                    nsel = min(2 * nsel, nb)
+                    history.append((t, nsel))
+                    full = nsel >= nb
+            anchors.append(t)
+            anchor_t, f_anchor = t, f
             H_a, P_a = H.copy(), P.copy()
-            epoch_pos = 0 if full else 1
+            prev_exact = f
         else:
             blocks = sample_blocks(seed, t, nb, nsel)
             P = svrg_sh_estimate(S, H, H_a, P_a, blocks, block_rows)
             fs.append(float("nan"))
             prev_exact = None
-            epoch_pos += 1
-            if epoch_pos >= E:
-                epoch_pos = 0
-        g = 4.0 * (H @ K - P)
+        g = 4.0 * (H @ (H.T @ H) - P)
         H, G = _step(H, G, g, lr, eps, rho)
         t += 1
-    return dict(H=H, G=G, f=fs, iters=t, converged=converged, history=history,
+    out_state = dict(t=t, nsel=nsel, anchor_t=anchor_t, f_anchor=f_anchor, H_a=H_a, P_a=P_a,
+                     f_prev=prev_exact)
+    return dict(H=H, G=G, f=fs, iters=t - t0, converged=converged, history=history,
                 gamma=gamma, start_branch=start_branch,
-                final_branch="full" if full else "sampled", nsel=nsel)
+                final_branch="full" if full else "sampled", nsel=nsel, anchors=anchors,
+                state=out_state)
 
 
 # --------------------------------------------------------------------------
