@@ -42,7 +42,7 @@ extern "C" {
 #endif
 #pragma GCC visibility push(default)
 
-#define SYMNMF_ABI_VERSION 4
+#define SYMNMF_ABI_VERSION 5
 
 enum symnmf_status {
     SYMNMF_OK = 0,
@@ -63,7 +63,8 @@ enum symnmf_solver { SYMNMF_AUTO = 0, SYMNMF_FULL = 1, SYMNMF_BLOCK_SVRG = 2 };
 /* The S.H product of the fit's full-batch steps and anchor refreshes.
  * ROWS streams all of S in row panels (symnmf_sh). UPPER reads only the 32 x 32
  * blocks on or above the diagonal, each serving both of its products
- * (symnmf_sh_sym; P1 "Factorization at scale", "The problem": S = S^T): half
+ * (symnmf_sh_sym; P1 "Factorization at scale"; S = S^T since P1's introduction
+ * defines S as an absolute correlation or a TPDM, both symmetric): half
  * the bytes of S per step, for k <= 32, with a workspace larger by about
  * k n^2 / 256 bytes. The Block-SVRG sampled steps read row panels either way. */
 enum symnmf_sh_pass { SYMNMF_SH_ROWS = 0, SYMNMF_SH_UPPER = 1 };
@@ -100,8 +101,9 @@ typedef struct symnmf_fit_params {
     double phi0;           /* > 0: initial sampled fraction, |B|0 = ceil(phi0 nb);
                               <= 0: seeded from gamma_{k+1}                              */
     double gap_threshold;  /* gamma_{k+1} >= this selects the full gradient; default 5  */
-    double tol_rel;        /* stop when |f_{t-1} - f_t| < tol_rel |f_{t-1}|; 0 = never;
-                              default 1e-6                                               */
+    double tol_rel;        /* stop when |f_{t-1} - f_t| < tol_rel max(|f_{t-1}|,
+                              obj_floor ||S||^2) (full batch; per step of the epoch
+                              between Block-SVRG anchors); 0 = never; default 1e-6       */
     double stall_tol;      /* sampled branch: anchor objective decrease below
                               stall_tol * previous anchor doubles |B|; default 1e-3     */
     double init_scale;     /* INIT_UNIFORM scale; default 0.1                           */
@@ -115,10 +117,32 @@ typedef struct symnmf_fit_params {
                               projected step is unchanged. Applies to every step.      */
     int32_t sh_pass;       /* enum symnmf_sh_pass: the S.H product of the full-batch
                               steps and anchors; default ROWS                           */
+    double obj_floor;      /* the stop test's denominator never falls below
+                              obj_floor ||S||^2; default 0.05 (>= 0)                     */
+    int32_t start_iter;    /* absolute step index of the entry H: the Block-SVRG block
+                              lists of step t are drawn for start_iter + t; default 0;
+                              with resume = 1 and a state, it must equal state->iter  */
 } symnmf_fit_params;
 
+/* The AdaptGrow controller's state at a returned H, for resuming a fit so that
+ * the resumed call takes the same steps as one uninterrupted call. Host
+ * struct; the two anchor buffers are caller-owned device arrays (n x k, ld k),
+ * both required whenever a state is passed. symnmf_fit writes the state of the
+ * H it returns (iter = start_iter + iterations) and reads it when resume = 1. */
+typedef struct symnmf_fit_state {
+    int32_t iter;          /* absolute step index of H                              */
+    int32_t blocks;        /* |B|; n_blocks means the full-batch branch              */
+    int32_t anchor_iter;   /* absolute step of the current Block-SVRG anchor; -1: none */
+    int32_t f_prev_valid;  /* 1: f_prev is the exact objective of step iter - 1     */
+    double f_anchor;       /* exact objective at anchor_iter                          */
+    double f_prev;
+    float* H_anchor;       /* device: H~, the anchor's H                             */
+    float* P_anchor;       /* device: P~ = S H~                                      */
+} symnmf_fit_state;
+
 typedef struct symnmf_fit_report {
-    int32_t iterations;     /* update steps taken; H returned is H_iterations           */
+    int32_t iterations;     /* update steps taken in this call; H returned is
+                               H_{start_iter + iterations}                               */
     int32_t converged;      /* 1 if the tol_rel test stopped the run                    */
     int32_t start_branch;   /* 0 full batch, 1 Block-SVRG                               */
     int32_t final_branch;
@@ -126,7 +150,7 @@ typedef struct symnmf_fit_report {
     int32_t n_blocks;       /* nb = ceil(n / block_rows)                                */
     int32_t doublings;      /* number of |B| doublings                                  */
     int32_t zero_rows;      /* rows of the returned H that are all zero (label 0)       */
-    int32_t f_last_iter;    /* step index of f_last                                     */
+    int32_t f_last_iter;    /* step index of f_last within this call (its obj_trace)    */
     int32_t anchors;        /* Block-SVRG anchor refreshes                              */
     double gamma;           /* gamma_{k+1} used for the branch choice (NaN if unused)   */
     double lr_used;
@@ -198,7 +222,8 @@ int symnmf_sh(const float* S, int64_t n, int64_t lds, const float* H, int32_t k,
               float* P, double* tr_host, void* ws, size_t ws_bytes, void* hip_stream);
 
 /* The S.H pass from the upper triangle (P1 "Factorization at scale": the
- * S H products dominate; P1 "The problem": S is symmetric). Same contract as
+ * S H products dominate; P1 introduction: S, an absolute correlation or a
+ * TPDM, is symmetric by definition). Same contract as
  * symnmf_sh (P = S H, n x k, ld k; tr_host nullable) for 1 <= k <= 32, but
  * it reads only the 32 x 32 blocks of S on or above the diagonal, each once
  * (2 n^2 bytes instead of 4 n^2): an off-diagonal block S_ab adds S_ab H_b to
@@ -232,11 +257,18 @@ int symnmf_sq(const float* S, int64_t n, int64_t lds, const float* Q, int32_t w,
  * Objective f(H) = ||S||^2 - 2 tr(H^T S H) + ||H^T H||^2 = ||S - H H^T||_F^2,
  * evaluated without n x n intermediates (P1 "Factorization at scale").
  * Full-batch step t: P = S H_t, f_t, stop test, g = 4 (H_t (H_t^T H_t) - P),
- * G += g*g, H_{t+1} = max(H_t - lr g/(sqrt(G) + eps), 0).
+ * G += g*g, H_{t+1} = max(H_t - lr g/(sqrt(G) + eps), 0). The stop test ends
+ * the run at H_t when |f_{t-1} - f_t| < tol_rel max(|f_{t-1}|, obj_floor
+ * ||S||^2) (a relative change; the floor keeps it meaningful when S can be
+ * factored almost exactly and f tends to zero, as for a TPDM of rank below k).
  * Block-SVRG steps replace P by P~ + (nb/|B|) sum_{rows i in B} S[i,:]^T
- * (H - H~)[i,:] over |B| sampled row blocks; anchors (H~, P~ = S H~) refresh
- * every ceil(nb/|B|) steps, and an anchor objective that fell by less than
- * stall_tol doubles |B| until the run is full batch (AUTO and BLOCK_SVRG).
+ * (H - H~)[i,:] over |B| sampled row blocks (B drawn for the absolute step
+ * index); a step is an anchor (H~ = H_t, P~ = S H_t, f exact, exact gradient)
+ * when ceil(nb/|B|) steps have passed since the last one. At an anchor E_j
+ * steps after the previous one: |f~prev - f~| < tol_rel E_j max(|f~prev|,
+ * obj_floor ||S||^2) stops the run at this H (converged); otherwise a
+ * decrease below stall_tol f~prev doubles |B|, until the run is full batch
+ * (AUTO and BLOCK_SVRG), G kept.
  * AUTO chooses the branch from gamma_{k+1} = lambda_{k+1}/|lambda_{k+2}| of
  * eigvals_host (>= gap_threshold: full; else |B|0 = 2^floor(log2(max(1,
  * gamma/gap_threshold nb)))), unless phi0 > 0. The denominator is floored at
@@ -244,17 +276,23 @@ int symnmf_sq(const float* S, int64_t n, int64_t lds, const float* Q, int32_t w,
  * |lambda| when used.
  * H (n x k): output (and input for INIT_CALLER). G (nullable, n x k): receives
  * the accumulator of the returned H (input too when resume = 1).
- * obj_trace_host (nullable): f_t for t < min(obj_trace_cap, steps evaluated);
- * NaN for Block-SVRG steps (f is exact only at anchors).
+ * obj_trace_host (nullable): f_t for the steps of this call, t < min(
+ * obj_trace_cap, steps evaluated); NaN for Block-SVRG steps (f is exact only at
+ * anchors).
  * rep_host (nullable): the report.
+ * state (nullable, host): the controller state of the returned H, written on
+ * every successful return; with resume = 1 also read on entry (branch, |B|,
+ * anchor, previous objectives), which skips the branch choice. Without a
+ * state, resume = 1 restores only G (exact for full-batch runs without a stop
+ * test).
  * Requires S symmetric and nonnegative, 1 <= k <= 64, k <= n.
  * Returns OK, W_NOT_CONVERGED, or E_INVALID / E_WORKSPACE / E_NONFINITE /
  * E_HIP. */
 int symnmf_fit(const float* S, int64_t n, int64_t lds, int32_t k,
                const symnmf_fit_params* prm, const double* eigvals_host,
                int32_t n_eig, float* H, float* G, double* obj_trace_host,
-               int32_t obj_trace_cap, symnmf_fit_report* rep_host, void* ws,
-               size_t ws_bytes, void* hip_stream);
+               int32_t obj_trace_cap, symnmf_fit_report* rep_host,
+               symnmf_fit_state* state, void* ws, size_t ws_bytes, void* hip_stream);
 
 /* Hard labels (P1 "Factorizing with SymNMF": the row-wise argmax of H):
  * labels[i] = argmax_c H[i, c], lowest index on ties; an all-zero row gets 0.

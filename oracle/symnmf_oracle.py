@@ -268,7 +268,7 @@ def converged_test(f_prev, f, tol, steps, floor_abs):
 
 
 def fit_full(S, H0, lr, max_iters, tol=0.0, eps=1e-8, G0=None, objective="trace", rho=0.0,
-             obj_floor=0.05):
+             obj_floor=0.05, snapshots=()):
     """Full-batch projected AdaGrad (RMSprop's accumulator when rho > 0).
 
     Iteration t: P = S H_t; f_t = f(H_t) (before the update); if t >= 1 and
@@ -276,7 +276,8 @@ def fit_full(S, H0, lr, max_iters, tol=0.0, eps=1e-8, G0=None, objective="trace"
     return H_t; otherwise take the AdaGrad step. At most ``max_iters`` steps.
     ``objective`` "explicit" evaluates f as ||S - H H^T||^2 directly, "trace"
     by the identity ||S||^2 - 2 tr(H^T P) + ||H^T H||^2.
-    Returns dict(H, G, f (list of f_t), iters (steps taken), converged).
+    Returns dict(H, G, f (list of f_t), iters (steps taken), converged, H_at
+    (a copy of H_t for every t in ``snapshots`` that the run reaches)).
     """
     S = np.asarray(S, dtype=np.float64)
     H = np.array(H0, dtype=np.float64)
@@ -284,8 +285,11 @@ def fit_full(S, H0, lr, max_iters, tol=0.0, eps=1e-8, G0=None, objective="trace"
     s2 = float(np.einsum("ij,ij->", S, S))  # ||S||_F^2 without an n x n temporary
     fs = []
     converged = False
+    H_at = {}
     t = 0
     while t < max_iters:
+        if t in snapshots:
+            H_at[t] = H.copy()
         P = S @ H
         f = objective_trace(s2, H, P) if objective == "trace" else objective_explicit(S, H)
         fs.append(f)
@@ -295,7 +299,9 @@ def fit_full(S, H0, lr, max_iters, tol=0.0, eps=1e-8, G0=None, objective="trace"
         g = 4.0 * (H @ (H.T @ H) - P)
         H, G = _step(H, G, g, lr, eps, rho)
         t += 1
-    return dict(H=H, G=G, f=fs, iters=t, converged=converged)
+    if t in snapshots:
+        H_at[t] = H.copy()
+    return dict(H=H, G=G, f=fs, iters=t, converged=converged, H_at=H_at)
 
 
 # --------------------------------------------------------------------------
@@ -358,7 +364,7 @@ def initial_blocks(gamma, nb, threshold=5.0):
 def fit_adaptgrow(S, H0, lr, max_iters, *, solver=SOLVER_AUTO, eigvals=None, k=None,
                   phi0=0.0, block_rows=1024, gap_threshold=5.0, tol=1e-6,
                   stall_tol=1e-3, obj_floor=0.05, eps=1e-8, seed=0, rho=0.0,
-                  objective="trace", G0=None, state=None):
+                  objective="trace", G0=None, state=None, snapshots=()):
     """AdaptGrow: full-batch AdaGrad or Block-SVRG with sample growth.
 
     Branch choice: FULL -> full; otherwise |B|0 from phi0 > 0
@@ -385,7 +391,8 @@ def fit_adaptgrow(S, H0, lr, max_iters, *, solver=SOLVER_AUTO, eigvals=None, k=N
     uninterrupted call. ``max_iters`` counts the steps of this call.
     Returns dict(H, G, f (this call's f_t), iters (steps taken in this call),
     converged, history [(t, |B|) at each doubling, absolute t], gamma,
-    start_branch, final_branch, nsel, anchors (absolute steps), state).
+    start_branch, final_branch, nsel, anchors (absolute steps), state, H_at (a
+    copy of H_t for every absolute t in ``snapshots`` that the run reaches)).
     """
     S = np.asarray(S, dtype=np.float64)
     H = np.array(H0, dtype=np.float64)
@@ -429,9 +436,12 @@ def fit_adaptgrow(S, H0, lr, max_iters, *, solver=SOLVER_AUTO, eigvals=None, k=N
     fs = []
     history = []
     anchors = []
+    H_at = {}
     converged = False
     t0 = t
     while t < t0 + max_iters:
+        if t in snapshots:
+            H_at[t] = H.copy()
         E = -(-nb // nsel)
         if full:
             P = S @ H
@@ -465,12 +475,14 @@ def fit_adaptgrow(S, H0, lr, max_iters, *, solver=SOLVER_AUTO, eigvals=None, k=N
         g = 4.0 * (H @ (H.T @ H) - P)
         H, G = _step(H, G, g, lr, eps, rho)
         t += 1
+    if t in snapshots:
+        H_at[t] = H.copy()
     out_state = dict(t=t, nsel=nsel, anchor_t=anchor_t, f_anchor=f_anchor, H_a=H_a, P_a=P_a,
                      f_prev=prev_exact)
     return dict(H=H, G=G, f=fs, iters=t - t0, converged=converged, history=history,
                 gamma=gamma, start_branch=start_branch,
                 final_branch="full" if full else "sampled", nsel=nsel, anchors=anchors,
-                state=out_state)
+                state=out_state, H_at=H_at)
 
 
 # --------------------------------------------------------------------------

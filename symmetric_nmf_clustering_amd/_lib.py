@@ -52,6 +52,22 @@ class FitParams(ctypes.Structure):
         ("resume", ctypes.c_int32),
         ("rms_decay", ctypes.c_double),
         ("sh_pass", ctypes.c_int32),
+        ("obj_floor", ctypes.c_double),
+        ("start_iter", ctypes.c_int32),
+    ]
+
+
+class FitState(ctypes.Structure):
+    """symnmf_fit_state: the controller state at a returned H (resumption)."""
+    _fields_ = [
+        ("iter", ctypes.c_int32),
+        ("blocks", ctypes.c_int32),
+        ("anchor_iter", ctypes.c_int32),
+        ("f_prev_valid", ctypes.c_int32),
+        ("f_anchor", ctypes.c_double),
+        ("f_prev", ctypes.c_double),
+        ("H_anchor", ctypes.c_void_p),
+        ("P_anchor", ctypes.c_void_p),
     ]
 
 
@@ -105,8 +121,8 @@ SIGNATURES = [
      [_P, _I64, _I64, _P, _I32, _P, _P, ctypes.c_size_t, _P]),
     ("symnmf_fit", ctypes.c_int,
      [_P, _I64, _I64, _I32, ctypes.POINTER(FitParams), ctypes.POINTER(_D), _I32,
-      _P, _P, ctypes.POINTER(_D), _I32, ctypes.POINTER(FitReport), _P,
-      ctypes.c_size_t, _P]),
+      _P, _P, ctypes.POINTER(_D), _I32, ctypes.POINTER(FitReport), ctypes.POINTER(FitState),
+      _P, ctypes.c_size_t, _P]),
     ("symnmf_labels", ctypes.c_int, [_P, _I64, _I32, _P, _P]),
     ("symnmf_spherical_kmeans", ctypes.c_int,
      [_P, _I64, _I64, _I32, _I32, ctypes.c_uint64, _P, _P, ctypes.POINTER(_I32),

@@ -166,12 +166,27 @@ def sq(S: torch.Tensor, Q: torch.Tensor) -> torch.Tensor:
 
 
 @dataclass
+class FitState:
+    """The AdaptGrow controller state at a returned H: pass it back with that H
+    and G (``fit(..., H0=H, G0=G, state=...)``) to continue the run exactly."""
+    iter: int
+    blocks: int
+    anchor_iter: int
+    f_prev_valid: int
+    f_anchor: float
+    f_prev: float
+    H_anchor: torch.Tensor
+    P_anchor: torch.Tensor
+
+
+@dataclass
 class FitResult:
     H: torch.Tensor
     G: Optional[torch.Tensor]
     report: dict
     f_trace: np.ndarray
     status: int
+    state: Optional[FitState] = None
 
     @property
     def converged(self) -> bool:
@@ -197,18 +212,26 @@ def fit_params(**kw) -> L.FitParams:
 
 def fit(S: torch.Tensor, k: int, *, eigvals=None, H0: Optional[torch.Tensor] = None,
         G0: Optional[torch.Tensor] = None, return_G: bool = False,
-        trace_cap: Optional[int] = None, ws: Optional[torch.Tensor] = None, **params) -> FitResult:
+        trace_cap: Optional[int] = None, ws: Optional[torch.Tensor] = None,
+        state: Optional[FitState] = None, return_state: bool = False, **params) -> FitResult:
     """SymNMF fit S ~ H H^T with projected AdaGrad / Block-SVRG AdaptGrow.
 
     ``params`` are the fields of symnmf_fit_params (solver, max_iters, lr, eps,
     block_rows, init, phi0, gap_threshold, tol_rel, stall_tol, init_scale,
-    seed, check_every, rms_decay, sh_pass). H0 sets init='caller'; G0 sets
-    resume=1."""
+    seed, check_every, rms_decay, sh_pass, obj_floor, start_iter). H0 sets
+    init='caller'; G0 sets resume=1. ``state`` (a previous result's state,
+    with its H as H0 and G as G0) restores the controller and sets start_iter;
+    ``return_state`` asks for the state of the returned H."""
     n, lds = _S_layout(S)
     if H0 is not None:
-        params.setdefault("init", L.INIT_CALLER)
+        if params.setdefault("init", L.INIT_CALLER) not in (L.INIT_CALLER, "caller"):
+            raise ValueError("H0 given with an init other than 'caller'")
     if G0 is not None:
         params["resume"] = 1
+    if state is not None:
+        if G0 is None:
+            raise ValueError("resuming from a state needs G0")
+        params["start_iter"] = state.iter
     p = fit_params(**params)
     H = torch.empty((n, k), dtype=torch.float32, device=S.device)
     if H0 is not None:
@@ -232,13 +255,31 @@ def fit(S: torch.Tensor, k: int, *, eigvals=None, H0: Optional[torch.Tensor] = N
     need = workspace_bytes(L.OP_FIT, n, k, 0, p)
     if ws is None or ws.numel() < need:
         ws = workspace(need, S.device)
+    cst = None
+    Ha_out = Pa_out = None
+    if state is not None or return_state:
+        Ha_out = torch.empty((n, k), dtype=torch.float32, device=S.device)
+        Pa_out = torch.empty((n, k), dtype=torch.float32, device=S.device)
+        cst = L.FitState()
+        if state is not None:
+            for name in ("iter", "blocks", "anchor_iter", "f_prev_valid", "f_anchor", "f_prev"):
+                setattr(cst, name, getattr(state, name))
+            Ha_out.copy_(state.H_anchor)
+            Pa_out.copy_(state.P_anchor)
+        cst.H_anchor = Ha_out.data_ptr()
+        cst.P_anchor = Pa_out.data_ptr()
     st = lib.symnmf_fit(_ptr(S), n, lds, k, ctypes.byref(p), ev, n_eig, _ptr(H), _ptr(G),
-                        trace if cap > 0 else None, cap, ctypes.byref(rep), _ptr(ws), ws.numel(),
+                        trace if cap > 0 else None, cap, ctypes.byref(rep),
+                        ctypes.byref(cst) if cst is not None else None, _ptr(ws), ws.numel(),
                         ctypes.c_void_p(_stream_ptr()))
     L.check(st, "symnmf_fit")
     r = rep.as_dict()
     ncopy = min(cap, r["iterations"] + (1 if r["converged"] else 0))
-    return FitResult(H, G, r, np.array(trace[:ncopy], dtype=np.float64), st)
+    out_state = None
+    if cst is not None:
+        out_state = FitState(cst.iter, cst.blocks, cst.anchor_iter, cst.f_prev_valid,
+                             cst.f_anchor, cst.f_prev, Ha_out, Pa_out)
+    return FitResult(H, G, r, np.array(trace[:ncopy], dtype=np.float64), st, out_state)
 
 
 def labels(H: torch.Tensor) -> torch.Tensor:

@@ -36,18 +36,39 @@ def hipcc() -> str:
 
 
 def build(verbose: bool = False) -> str:
+    """Compiles every source to an object in parallel (one hipcc per file, in
+    _build/ at the repository root), then links libsymnmf.so."""
     os.makedirs(OUT_DIR, exist_ok=True)
+    obj_dir = os.path.join(ROOT, "_build")
+    os.makedirs(obj_dir, exist_ok=True)
+    compile_flags = [f for f in FLAGS if f != "-shared"]
+    procs = []
+    objs = []
+    for src in SOURCES:
+        obj = os.path.join(obj_dir, src + ".o")
+        objs.append(obj)
+        cmd = [hipcc(), *compile_flags, "-c", "-I", os.path.join(ROOT, "include"), "-I", HERE,
+               os.path.join(HERE, src), "-o", obj]
+        if verbose:
+            print(" ".join(cmd), flush=True)
+        procs.append((src, subprocess.Popen(cmd, stdout=subprocess.PIPE, stderr=subprocess.PIPE,
+                                            text=True)))
+    failed = []
+    for src, pr in procs:
+        out, err = pr.communicate()
+        if pr.returncode != 0:
+            failed.append(src)
+            sys.stderr.write(out + err)
+        elif verbose and err.strip():
+            sys.stderr.write(err)
+    if failed:
+        raise RuntimeError("hipcc failed on " + ", ".join(failed))
     tmp = OUT + ".tmp"
-    cmd = [hipcc(), *FLAGS, "-I", os.path.join(ROOT, "include"), "-I", HERE,
-           *[os.path.join(HERE, s) for s in SOURCES], "-o", tmp]
-    if verbose:
-        print(" ".join(cmd), flush=True)
+    cmd = [hipcc(), "--offload-arch=gfx950", "-shared", "-fPIC", *objs, "-o", tmp]
     res = subprocess.run(cmd, capture_output=True, text=True)
     if res.returncode != 0:
         sys.stderr.write(res.stdout + res.stderr)
-        raise RuntimeError("hipcc failed building libsymnmf.so")
-    if verbose and res.stderr.strip():
-        sys.stderr.write(res.stderr)
+        raise RuntimeError("hipcc failed linking libsymnmf.so")
     os.replace(tmp, OUT)
     return OUT
 

@@ -285,7 +285,7 @@ __global__ __launch_bounds__(256) void finalize_finish_kernel(FitDev* fd, double
                 fd->done = 1;
                 fd->stop_iter = t;
             } else if ((flags & 2) && fd->tol > 0.0 && fd->f_prev_valid &&
-                       fabs(fd->f_prev - f) < fd->tol * fabs(fd->f_prev)) {
+                       fabs(fd->f_prev - f) < fd->tol * fmax(fabs(fd->f_prev), fd->floor_abs)) {
                 fd->status = 1;
                 fd->done = 1;
                 fd->stop_iter = t;
@@ -340,7 +340,9 @@ __global__ __launch_bounds__(256) void block_diff_kernel(const float* __restrict
                                                          const float* __restrict__ Ha,
                                                          const int* __restrict__ blocks,
                                                          int block_rows, int n, int k,
-                                                         float* __restrict__ D) {
+                                                         float* __restrict__ D,
+                                                         const int* __restrict__ done) {
+    if (done && *done) return;
     const int64_t base = (int64_t)blocks[blockIdx.y] * block_rows;
     const int64_t end = min((int64_t)n, base + block_rows) * k;
     for (int64_t e = base * k + (int64_t)blockIdx.x * 256 + threadIdx.x; e < end;
@@ -349,12 +351,13 @@ __global__ __launch_bounds__(256) void block_diff_kernel(const float* __restrict
 }
 
 hipError_t launch_block_diff(const float* H, const float* Ha, const int* blocks, int nsel,
-                             int block_rows, int n, int k, float* D, hipStream_t st) {
+                             int block_rows, int n, int k, float* D, const int* done,
+                             hipStream_t st) {
     if (nsel <= 0) return hipSuccess;
     const int64_t per = (int64_t)block_rows * k;
     const unsigned gx = (unsigned)std::min<int64_t>(64, (per + 255) / 256);
     hipLaunchKernelGGL(block_diff_kernel, dim3(gx, (unsigned)nsel), dim3(256), 0, st, H, Ha,
-                       blocks, block_rows, n, k, D);
+                       blocks, block_rows, n, k, D, done);
     return hipGetLastError();
 }
 

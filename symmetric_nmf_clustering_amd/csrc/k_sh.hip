@@ -86,6 +86,7 @@ __global__ __launch_bounds__(256) void sh_panel_kernel(const float* __restrict__
                                                        const float* __restrict__ X, int width_arg,
                                                        RowPlan rp, int nsplit,
                                                        float* __restrict__ part, int ldp_arg) {
+    if (rp.done && *rp.done) return;  // uniform over the workgroup
     const int width = XVEC ? 16 * NCM + NV : width_arg;
     const int ldp = XVEC ? 16 * NCM + NV : ldp_arg;
     constexpr int U = sh_rows_per_trip(NCM, NV, CW, RM);
@@ -331,6 +332,7 @@ __global__ __launch_bounds__(256) void sh_ring_kernel(const float* __restrict__ 
                                                       const float* __restrict__ X, int width,
                                                       RowPlan rp, float* __restrict__ part,
                                                       int ldp) {
+    if (rp.done && *rp.done) return;  // uniform over the workgroup
     constexpr int WMAX = 16 * NCM + NV;
     constexpr int NXI = sh_ring_xdma(NCM, NV);
     constexpr int PER = 1 + NXI;                 // DMA instructions per trip and wave

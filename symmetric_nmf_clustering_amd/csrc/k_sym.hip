@@ -1,7 +1,8 @@
 // The symmetric S.H pass: P = S H from the upper triangle of S alone. The
 // S H products are the dominant cost of the fit (P1 "Factorization at scale"),
-// and S = S^T by construction (P1 "The problem"), so every off-diagonal
-// element can serve both of the products it takes part in.
+// and S = S^T by definition (P1 introduction: S is an absolute Pearson
+// correlation or a tail pairwise dependence matrix, both symmetric in i, j), so
+// every off-diagonal element can serve both of the products it takes part in.
 //
 // S is cut into 32 x 32 blocks; block (a, b) holds rows 32a..32a+31 and
 // columns 32b..32b+31. The pass uses the blocks with a <= b, once each. A
@@ -69,7 +70,9 @@ __device__ __forceinline__ uint32_t pack_hi(float a, float b) {
 // Rows >= n and columns >= k are zero.
 __global__ __launch_bounds__(256) void sym_pack_kernel(const float* __restrict__ H, int n, int k,
                                                        int NT, int nkb, int rowmap,
-                                                       u32x4* __restrict__ out) {
+                                                       u32x4* __restrict__ out,
+                                                       const int* __restrict__ done) {
+    if (done && *done) return;
     const int64_t t = (int64_t)blockIdx.x * 256 + threadIdx.x;
     if (t >= (int64_t)nkb * NT * 64) return;
     const int lane = (int)(t & 63);
@@ -95,7 +98,9 @@ __global__ __launch_bounds__(256) void sym_pack_kernel(const float* __restrict__
 template <int NT>
 __global__ __launch_bounds__(64 * kSymWaves) void sym_kernel(
     const float* __restrict__ S, int64_t lds, const u32x4* __restrict__ HsR,
-    const u32x4* __restrict__ HsC, int n, int k, float* __restrict__ P1, float* __restrict__ P2) {
+    const u32x4* __restrict__ HsC, int n, int k, float* __restrict__ P1, float* __restrict__ P2,
+    const int* __restrict__ done) {
+    if (done && *done) return;  // uniform over the workgroup, before any barrier
     constexpr int WAVES = kSymWaves;
     constexpr int NTH = 64 * WAVES;
     constexpr int HB = NT * 3 * 64;  // 16-byte pieces of one packed K block of H
@@ -343,7 +348,9 @@ __global__ __launch_bounds__(256) void sym_fold_kernel(const float* __restrict__
                                                        const float* __restrict__ P2, int n, int k,
                                                        int NS, float* __restrict__ P, int ldP,
                                                        const float* __restrict__ Hdot,
-                                                       double* __restrict__ tr_part) {
+                                                       double* __restrict__ tr_part,
+                                                       const int* __restrict__ done) {
+    if (done && *done) return;
     __shared__ double redd[4];
     const int row0 = blockIdx.x * kUpdRows;
     const int rows = min(kUpdRows, n - row0);
@@ -392,13 +399,13 @@ SymPlan sym_plan(int n, int k) {
 }
 
 hipError_t launch_sym_pack(const float* H, int n, int k, const SymPlan& p, void* HsR, void* HsC,
-                           hipStream_t st) {
+                           const int* done, hipStream_t st) {
     for (int rowmap = 0; rowmap < 2; ++rowmap) {
         const int nkb = rowmap ? p.nkb_row : p.nkb_col;
         const int64_t threads = (int64_t)nkb * p.nt * 64;
         hipLaunchKernelGGL(sym_pack_kernel, dim3((unsigned)((threads + 255) / 256)), dim3(256), 0,
                            st, H, n, k, p.nt, nkb, rowmap,
-                           static_cast<u32x4*>(rowmap ? HsR : HsC));
+                           static_cast<u32x4*>(rowmap ? HsR : HsC), done);
         const hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
@@ -406,17 +413,18 @@ hipError_t launch_sym_pack(const float* H, int n, int k, const SymPlan& p, void*
 }
 
 hipError_t launch_sym(const float* S, int64_t lds, const void* HsR, const void* HsC, int n, int k,
-                      const SymPlan& p, float* P1, float* P2, hipStream_t st) {
+                      const SymPlan& p, float* P1, float* P2, const int* done,
+                      hipStream_t st) {
     const u32x4* hr = static_cast<const u32x4*>(HsR);
     const u32x4* hc = static_cast<const u32x4*>(HsC);
     const dim3 grid((unsigned)p.ns, (unsigned)p.nq);
     const dim3 block(64 * kSymWaves);
     switch (p.nt) {
         case 1:
-            hipLaunchKernelGGL((sym_kernel<1>), grid, block, 0, st, S, lds, hr, hc, n, k, P1, P2);
+            hipLaunchKernelGGL((sym_kernel<1>), grid, block, 0, st, S, lds, hr, hc, n, k, P1, P2, done);
             break;
         case 2:
-            hipLaunchKernelGGL((sym_kernel<2>), grid, block, 0, st, S, lds, hr, hc, n, k, P1, P2);
+            hipLaunchKernelGGL((sym_kernel<2>), grid, block, 0, st, S, lds, hr, hc, n, k, P1, P2, done);
             break;
         default: return hipErrorInvalidValue;
     }
@@ -425,10 +433,10 @@ hipError_t launch_sym(const float* S, int64_t lds, const void* HsR, const void* 
 
 hipError_t launch_sym_fold(const float* P1, const float* P2, int n, int k, const SymPlan& p,
                            float* P, int ldP, const float* Hdot, double* tr_part,
-                           hipStream_t st) {
+                           const int* done, hipStream_t st) {
     const int nblk = (n + kUpdRows - 1) / kUpdRows;
     hipLaunchKernelGGL(sym_fold_kernel, dim3(nblk), dim3(256), 0, st, P1, P2, n, k, p.ns, P, ldP,
-                       Hdot, tr_part);
+                       Hdot, tr_part, done);
     return hipGetLastError();
 }
 

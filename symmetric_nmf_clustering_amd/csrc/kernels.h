@@ -32,6 +32,7 @@ struct RowPlan {
     int sub;
     int seg;
     int bps;
+    const int* done;  // nullable: a set flag (a fit that has stopped) skips the pass
 };
 
 // Device state of one fit, in the caller's workspace.
@@ -40,6 +41,7 @@ struct FitDev {
     double K2;          // ||H_t^T H_t||_F^2 for the current H_t
     double f_prev;      // last exact objective
     double tol;         // relative convergence tolerance (0: no test)
+    double floor_abs;   // the stop test's denominator is max(|f_prev|, floor_abs)
     int f_prev_valid;
     int done;           // once set, every later kernel of the fit returns at once
     int stop_iter;
@@ -95,17 +97,21 @@ struct SymPlan {
     size_t packed_row_bytes;
 };
 SymPlan sym_plan(int n, int k);
+// `done` (nullable, device): a set flag skips the launch's work (a fit that
+// has already stopped).
 hipError_t launch_sym_pack(const float* H, int n, int k, const SymPlan& p, void* HsR, void* HsC,
-                           hipStream_t st);
+                           const int* done, hipStream_t st);
 hipError_t launch_sym(const float* S, int64_t lds, const void* HsR, const void* HsC, int n, int k,
-                      const SymPlan& p, float* P1, float* P2, hipStream_t st);
+                      const SymPlan& p, float* P1, float* P2, const int* done, hipStream_t st);
 hipError_t launch_sym_fold(const float* P1, const float* P2, int n, int k, const SymPlan& p,
-                           float* P, int ldP, const float* Hdot, double* tr_part, hipStream_t st);
+                           float* P, int ldP, const float* Hdot, double* tr_part, const int* done,
+                           hipStream_t st);
 // D[j][c] = H[j][c] - Ha[j][c] (fp32) for the rows j of the nsel listed row
 // blocks of block_rows rows (the Block-SVRG correction's input); other rows
 // of D are left as they are.
 hipError_t launch_block_diff(const float* H, const float* Ha, const int* blocks, int nsel,
-                             int block_rows, int n, int k, float* D, hipStream_t st);
+                             int block_rows, int n, int k, float* D, const int* done,
+                             hipStream_t st);
 // P[i][c] = sum_s part[s][i][c] (c < width, ld width); if Hdot: tr_part[b] =
 // sum over the rows of block b of <Hdot_i, P_i> (fp64). Blocks of kUpdRows rows.
 hipError_t launch_reduce_partials(const float* part, int nsplit, int n, int width, int ldp,

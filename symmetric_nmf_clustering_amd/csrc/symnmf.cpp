@@ -53,6 +53,7 @@ struct ProfEntry {
     hipEvent_t a, b;
     int which;
     double bytes;
+    int64_t tag;  // -1, or (fit call << 32 | step) for launches a stopped fit may skip
 };
 struct Prof {
     std::mutex mu;
@@ -72,7 +73,9 @@ struct ProfScope {
     hipStream_t st;
     int which;
     double bytes;
-    ProfScope(int w, double by, hipStream_t s) : st(s), which(w), bytes(by) {
+    int64_t tag;
+    ProfScope(int w, double by, hipStream_t s, int64_t tg = -1)
+        : st(s), which(w), bytes(by), tag(tg) {
         Prof& p = prof();
         if (!p.on) return;
         if (hipEventCreate(&a) != hipSuccess) {
@@ -91,7 +94,7 @@ struct ProfScope {
         (void)hipEventRecord(b, st);
         Prof& p = prof();
         std::lock_guard<std::mutex> g(p.mu);
-        p.pending.push_back({a, b, which, bytes});
+        p.pending.push_back({a, b, which, bytes, tag});
     }
 };
 
@@ -111,6 +114,27 @@ void prof_drain() {
     }
     p.pending.clear();
 }
+
+// Drops the pending timings tagged [lo, hi]: launches a fit enqueued after its
+// device stop flag was set, which returned without doing their work (their
+// durations would pull the kernels' averages down).
+void prof_discard(int64_t lo, int64_t hi) {
+    Prof& p = prof();
+    std::lock_guard<std::mutex> g(p.mu);
+    size_t keep = 0;
+    for (size_t i = 0; i < p.pending.size(); ++i) {
+        ProfEntry& e = p.pending[i];
+        if (e.tag >= lo && e.tag <= hi) {
+            (void)hipEventSynchronize(e.b);
+            (void)hipEventDestroy(e.a);
+            (void)hipEventDestroy(e.b);
+        } else {
+            p.pending[keep++] = e;
+        }
+    }
+    p.pending.resize(keep);
+}
+std::atomic<int64_t> g_fit_calls{0};
 
 #define HIPCHK(x)                                   \
     do {                                            \
@@ -441,7 +465,7 @@ size_t probe_layout(void* ws, int64_t n, int p, ProbeLayout* L) {
 struct FitLayout {
     FitDev* fd;
     double* f_trace;
-    float *Hb[2], *Gb[2], *Ha, *Pa, *D, *part, *gram_part;
+    float *Hb[2], *Gb[2], *Ha[2], *Pa[2], *D, *part, *gram_part;
     void *sym_hsr, *sym_hsc;  // upper-triangle pass (sh_pass UPPER only)
     float *sym_p1, *sym_p2;
     double *tr_part, *stats_part, *stats_out;
@@ -457,8 +481,8 @@ size_t fit_layout(void* ws, int64_t n, int k, int max_iters, int block_rows, int
     l.f_trace = c.take<double>((size_t)std::max(1, max_iters));
     for (int i = 0; i < 2; ++i) l.Hb[i] = c.take<float>((size_t)n * k);
     for (int i = 0; i < 2; ++i) l.Gb[i] = c.take<float>((size_t)n * k);
-    l.Ha = c.take<float>((size_t)n * k);
-    l.Pa = c.take<float>((size_t)n * k);
+    for (int i = 0; i < 2; ++i) l.Ha[i] = c.take<float>((size_t)n * k);
+    for (int i = 0; i < 2; ++i) l.Pa[i] = c.take<float>((size_t)n * k);
     l.D = c.take<float>((size_t)n * k);
     l.part = c.take<float>((size_t)kMaxSplits * n * ldp_of(k));
     l.gram_part = c.take<float>((size_t)nblk * k * k);
@@ -549,6 +573,8 @@ void symnmf_fit_params_default(symnmf_fit_params* p) {
     p->resume = 0;
     p->rms_decay = 0.0;
     p->sh_pass = SYMNMF_SH_ROWS;
+    p->obj_floor = 0.05;
+    p->start_iter = 0;
 }
 
 size_t symnmf_workspace_bytes(int op, int64_t n, int32_t k_or_p, int64_t T,
@@ -680,12 +706,12 @@ int symnmf_sh_sym(const float* S, int64_t n, int64_t lds, const float* H, int32_
     sym_layout(ws, n, k, &L);
     hipStream_t st = as_stream(hip_stream);
     const SymPlan sp = sym_plan((int)n, k);
-    HIPCHK(launch_sym_pack(H, (int)n, k, sp, L.hsr, L.hsc, st));
+    HIPCHK(launch_sym_pack(H, (int)n, k, sp, L.hsr, L.hsc, nullptr, st));
     {
         ProfScope ps(SYMNMF_PROF_SH_SYM, 2.0 * n * (double)(n + 1) + 8.0 * n * k, st);
-        HIPCHK(launch_sym(S, lds, L.hsr, L.hsc, (int)n, k, sp, L.p1, L.p2, st));
+        HIPCHK(launch_sym(S, lds, L.hsr, L.hsc, (int)n, k, sp, L.p1, L.p2, nullptr, st));
     }
-    HIPCHK(launch_sym_fold(L.p1, L.p2, (int)n, k, sp, P, k, H, L.tr_part, st));
+    HIPCHK(launch_sym_fold(L.p1, L.p2, (int)n, k, sp, P, k, H, L.tr_part, nullptr, st));
     if (tr_host) {
         HIPCHK(launch_sum_doubles(L.tr_part, cdiv(n, kUpdRows), L.tr_out, st));
         HIPCHK(hipMemcpyAsync(tr_host, L.tr_out, sizeof(double), hipMemcpyDeviceToHost, st));
@@ -934,7 +960,7 @@ void sample_blocks(uint64_t seed, int t, int nb, int nsel, std::vector<int>& per
 int symnmf_fit(const float* S, int64_t n, int64_t lds, int32_t k, const symnmf_fit_params* prm,
                const double* eigvals_host, int32_t n_eig, float* H, float* G,
                double* obj_trace_host, int32_t obj_trace_cap, symnmf_fit_report* rep_host,
-               void* ws, size_t ws_bytes, void* hip_stream) {
+               symnmf_fit_state* state, void* ws, size_t ws_bytes, void* hip_stream) {
     const auto t_start = std::chrono::steady_clock::now();
     symnmf_fit_params P;
     if (prm) P = *prm; else symnmf_fit_params_default(&P);
@@ -945,12 +971,25 @@ int symnmf_fit(const float* S, int64_t n, int64_t lds, int32_t k, const symnmf_f
         !(P.rms_decay >= 0.0 && P.rms_decay < 1.0) || P.sh_pass < 0 || P.sh_pass > 1 ||
         (P.sh_pass == SYMNMF_SH_UPPER && k > kSymMaxK) ||
         !(P.tol_rel >= 0.0) || !(P.stall_tol >= 0.0) || P.init < 0 || P.init > 2 ||
+        !(P.obj_floor >= 0.0) || !std::isfinite(P.obj_floor) || P.start_iter < 0 ||
+        (int64_t)P.start_iter + P.max_iters > INT32_MAX ||
         !(P.gap_threshold > 0.0) || (P.resume && !G) || (obj_trace_cap > 0 && !obj_trace_host) ||
         obj_trace_cap < 0 || !std::isfinite(P.lr) || !std::isfinite(P.phi0))
         return SYMNMF_E_INVALID;
     if (P.init == SYMNMF_INIT_UNIFORM && !(P.init_scale > 0.0)) return SYMNMF_E_INVALID;
     const int nb = (int)cdiv(n, P.block_rows);
-    const bool need_eig = P.solver != SYMNMF_FULL && !(P.phi0 > 0.0) && nb > 1;
+    const bool restore = P.resume && state;
+    if (state) {
+        if (!state->H_anchor || !state->P_anchor || !aligned(state->H_anchor, 4) ||
+            !aligned(state->P_anchor, 4))
+            return SYMNMF_E_INVALID;
+        if (restore && (state->iter != P.start_iter || state->blocks < 1 || state->blocks > nb ||
+                        state->anchor_iter > state->iter || state->anchor_iter < -1 ||
+                        (state->anchor_iter >= 0 && !std::isfinite(state->f_anchor)) ||
+                        (state->f_prev_valid && !std::isfinite(state->f_prev))))
+            return SYMNMF_E_INVALID;
+    }
+    const bool need_eig = !restore && P.solver != SYMNMF_FULL && !(P.phi0 > 0.0) && nb > 1;
     if (need_eig && (!eigvals_host || n_eig < k + 2)) return SYMNMF_E_INVALID;
     const size_t need = fit_layout(nullptr, n, k, P.max_iters, P.block_rows, P.sh_pass, nullptr);
     if (!ws_ok(ws, ws_bytes, need)) return SYMNMF_E_WORKSPACE;
@@ -961,6 +1000,8 @@ int symnmf_fit(const float* S, int64_t n, int64_t lds, int32_t k, const symnmf_f
     const int64_t nk = (int64_t)n * k;
     const int ldp = ldp_of(k);
     const int nblk = (int)cdiv(n, kUpdRows);
+    const int* done_dev = &L.fd->done;  // device address of the stop flag
+    const int64_t call_tag = (g_fit_calls.fetch_add(1) + 1) << 32;
 
     // ---- ||S||^2 and mean(S) (one pass over S)
     HIPCHK(launch_s_stats(S, lds, nn, L.stats_part, st));
@@ -971,6 +1012,7 @@ int symnmf_fit(const float* S, int64_t n, int64_t lds, int32_t k, const symnmf_f
     const double S_sum = stats[0], S_fro2 = stats[1];
     if (!std::isfinite(S_sum) || !std::isfinite(S_fro2)) return SYMNMF_E_NONFINITE;
     const double S_mean = S_sum / ((double)n * (double)n);
+    const double floor_abs = P.obj_floor * S_fro2;
 
     // ---- readings for the undefined scale-matched init and default lr
     const double a_sm = 2.0 * std::sqrt(std::max(0.0, S_mean) / k);
@@ -985,12 +1027,28 @@ int symnmf_fit(const float* S, int64_t n, int64_t lds, int32_t k, const symnmf_f
     if (P.resume) HIPCHK(launch_copy(L.Gb[0], G, nk, st));
     else HIPCHK(launch_fill(L.Gb[0], nk, 0.f, st));
 
+    // ---- controller state: fresh, or restored from the caller's state
+    int ab = 0;                // anchor buffer of the current anchor
+    int anchor_abs = -1;       // absolute step of the current anchor
+    double f_anchor = std::nan("");
+    if (restore && state->anchor_iter >= 0) {
+        anchor_abs = state->anchor_iter;
+        f_anchor = state->f_anchor;
+        HIPCHK(launch_copy(L.Ha[0], state->H_anchor, nk, st));
+        HIPCHK(launch_copy(L.Pa[0], state->P_anchor, nk, st));
+    }
+
     // ---- device state
     {
         FitDev h;
         std::memset(&h, 0, sizeof(h));
         h.S_fro2 = S_fro2;
         h.tol = P.tol_rel;
+        h.floor_abs = floor_abs;
+        if (restore && state->f_prev_valid) {
+            h.f_prev = state->f_prev;
+            h.f_prev_valid = 1;
+        }
         HIPCHK(hipMemcpyAsync(L.fd, &h, sizeof(FitDev), hipMemcpyHostToDevice, st));
         HIPCHK(hipStreamSynchronize(st));
     }
@@ -1006,7 +1064,9 @@ int symnmf_fit(const float* S, int64_t n, int64_t lds, int32_t k, const symnmf_f
     // ---- branch choice (P1 "Why this solver"; P2 sketch)
     double gamma = std::nan("");
     int nsel = nb;
-    if (P.solver == SYMNMF_FULL || nb <= 1) {
+    if (restore) {
+        nsel = state->blocks;
+    } else if (P.solver == SYMNMF_FULL || nb <= 1) {
         nsel = nb;
     } else if (P.phi0 > 0.0) {
         nsel = (int)std::min<int64_t>(nb, std::max<int64_t>(1, (int64_t)std::ceil(P.phi0 * nb - 1e-12)));
@@ -1017,31 +1077,34 @@ int symnmf_fit(const float* S, int64_t n, int64_t lds, int32_t k, const symnmf_f
     bool full = nsel >= nb;
     const int start_branch = full ? 0 : 1;
 
-    const FullPlan fpl = full_plan(nn);
+    FullPlan fpl = full_plan(nn);
+    fpl.rp.done = done_dev;
     const double sh_bytes = 4.0 * n * (double)n + 8.0 * (double)nk;
     const double sym_bytes = 2.0 * n * (double)(n + 1) + 8.0 * (double)nk;
+    const int T0 = P.start_iter;
     int cur = 0, t = 0, doublings = 0, anchors = 0, last_exact = -1;
-    double f_anchor_prev = std::nan("");
-    bool have_anchor_prev = false;
     FitDev hd;
     std::vector<int> perm, lists;
 
     const bool upper = P.sh_pass == SYMNMF_SH_UPPER;
     const SymPlan symp = sym_plan(nn, k);
-    auto exact_step = [&](bool write_anchor, int flags) -> int {
+    // one exact step at local index t (P_t = S H_t); with anchor >= 0 it also
+    // writes H~ = H_t, P~ = P_t into anchor buffer `anchor`
+    auto exact_step = [&](int anchor, int flags) -> int {
+        const int64_t tag = call_tag | t;
         if (upper) {
             // P_t = S H_t from the upper triangle, folded into the first
             // partial slot (the update then reads one partial)
-            HIPCHK(launch_sym_pack(L.Hb[cur], nn, k, symp, L.sym_hsr, L.sym_hsc, st));
+            HIPCHK(launch_sym_pack(L.Hb[cur], nn, k, symp, L.sym_hsr, L.sym_hsc, done_dev, st));
             {
-                ProfScope ps(SYMNMF_PROF_SH_SYM, sym_bytes, st);
+                ProfScope ps(SYMNMF_PROF_SH_SYM, sym_bytes, st, tag);
                 HIPCHK(launch_sym(S, lds, L.sym_hsr, L.sym_hsc, nn, k, symp, L.sym_p1, L.sym_p2,
-                                  st));
+                                  done_dev, st));
             }
             HIPCHK(launch_sym_fold(L.sym_p1, L.sym_p2, nn, k, symp, L.part, ldp, nullptr, nullptr,
-                                   st));
+                                   done_dev, st));
         } else {
-            ProfScope ps(SYMNMF_PROF_SH_FULL, sh_bytes, st);
+            ProfScope ps(SYMNMF_PROF_SH_FULL, sh_bytes, st, tag);
             HIPCHK(launch_sh_panel(S, lds, L.Hb[cur], k, fpl.rp, fpl.nsplit, L.part, ldp, st));
         }
         const int nsplit = upper ? 1 : fpl.nsplit;
@@ -1049,11 +1112,11 @@ int symnmf_fit(const float* S, int64_t n, int64_t lds, int32_t k, const symnmf_f
         a.n = nn; a.k = k; a.ldp = ldp; a.part = L.part; a.nsplit = nsplit;
         a.pstride = (int64_t)n * ldp; a.H = L.Hb[cur]; a.G = L.Gb[cur];
         a.Hn = L.Hb[cur ^ 1]; a.Gn = L.Gb[cur ^ 1];
-        a.Ha = write_anchor ? L.Ha : nullptr; a.Pa = write_anchor ? L.Pa : nullptr;
+        a.Ha = anchor >= 0 ? L.Ha[anchor] : nullptr; a.Pa = anchor >= 0 ? L.Pa[anchor] : nullptr;
         a.fd = L.fd; a.lr = (float)lr; a.eps = (float)P.eps; a.decay = (float)P.rms_decay;
         a.tr_part = L.tr_part; a.gram_part = L.gram_part;
         {
-            ProfScope ps(SYMNMF_PROF_UPDATE, (double)nk * 4.0 * (5 + nsplit), st);
+            ProfScope ps(SYMNMF_PROF_UPDATE, (double)nk * 4.0 * (5 + nsplit), st, tag);
             HIPCHK(launch_update(a, st));
         }
         HIPCHK(launch_finalize(L.fd, L.f_trace, t, nblk, k, L.tr_part, L.gram_part, flags, st));
@@ -1062,17 +1125,19 @@ int symnmf_fit(const float* S, int64_t n, int64_t lds, int32_t k, const symnmf_f
         return SYMNMF_OK;
     };
     auto sampled_step = [&](const int* blocks_dev) -> int {
-        const FullPlan sp = sampled_plan(nn, blocks_dev, nsel, P.block_rows);
+        FullPlan sp = sampled_plan(nn, blocks_dev, nsel, P.block_rows);
+        sp.rp.done = done_dev;
         {
             const double rows = std::min<double>((double)nsel * P.block_rows, (double)n);
             ProfScope ps(SYMNMF_PROF_SH_SAMPLED, 4.0 * rows * (double)n + 8.0 * (double)nk, st);
             // D = H - H~ on the sampled rows, then the correction sum over them
-            HIPCHK(launch_block_diff(L.Hb[cur], L.Ha, blocks_dev, nsel, P.block_rows, nn, k, L.D, st));
+            HIPCHK(launch_block_diff(L.Hb[cur], L.Ha[ab], blocks_dev, nsel, P.block_rows, nn, k,
+                                     L.D, done_dev, st));
             HIPCHK(launch_sh_panel(S, lds, L.D, k, sp.rp, sp.nsplit, L.part, ldp, st));
         }
         UpdateArgs a{};
         a.n = nn; a.k = k; a.ldp = ldp; a.part = L.part; a.nsplit = sp.nsplit;
-        a.pstride = (int64_t)n * ldp; a.Pt = L.Pa; a.pscale = (float)((double)nb / nsel);
+        a.pstride = (int64_t)n * ldp; a.Pt = L.Pa[ab]; a.pscale = (float)((double)nb / nsel);
         a.H = L.Hb[cur]; a.G = L.Gb[cur]; a.Hn = L.Hb[cur ^ 1]; a.Gn = L.Gb[cur ^ 1];
         a.fd = L.fd; a.lr = (float)lr; a.eps = (float)P.eps; a.decay = (float)P.rms_decay;
         a.gram_part = L.gram_part;
@@ -1092,47 +1157,64 @@ int symnmf_fit(const float* S, int64_t n, int64_t lds, int32_t k, const symnmf_f
     };
 
     int rc = SYMNMF_OK;
-    bool stopped = false;  // device stop flag seen
-    int cur_at_stop = 0;
+    bool stopped = false;         // device stop flag seen (full branch)
+    bool anchor_stop = false;     // the anchor stop test fired (sampled branch)
     // ---- Block-SVRG branch (P1 "Factorizing with SymNMF": SVRG-corrected
     // block-sampled gradient, sample grown toward the full gradient when
     // progress stalls)
     while (!full && t < P.max_iters) {
-        rc = exact_step(true, 1 | 4);
-        if (rc) return rc;
-        ++anchors;
-        last_exact = t - 1;
-        if ((rc = read_state())) return rc;
-        if (hd.status == -4) return SYMNMF_E_NONFINITE;
-        const double f = hd.f_prev;
-        if (have_anchor_prev && (f_anchor_prev - f) < P.stall_tol * f_anchor_prev) {
-            nsel = std::min(2 * nsel, nb);
-            ++doublings;
-            if (nsel >= nb) full = true;
-        }
-        f_anchor_prev = f;
-        have_anchor_prev = true;
-        if (full) break;
         const int E = (int)cdiv(nb, nsel);
-        const int steps = std::min(E - 1, P.max_iters - t);
-        if (steps <= 0) continue;
+        const int tabs = T0 + t;
+        if (anchor_abs < 0 || tabs - anchor_abs >= E) {
+            rc = exact_step(ab ^ 1, 1 | 4);
+            if (rc) return rc;
+            if ((rc = read_state())) return rc;
+            if (hd.status == -4) return SYMNMF_E_NONFINITE;
+            const double f = hd.f_prev;
+            if (anchor_abs >= 0) {
+                const int Ej = tabs - anchor_abs;
+                if (P.tol_rel > 0.0 &&
+                    std::fabs(f_anchor - f) < P.tol_rel * Ej * std::max(std::fabs(f_anchor), floor_abs)) {
+                    // converged: return H_t (the anchor's update went to the
+                    // other buffer and is dropped; the current anchor stays)
+                    anchor_stop = true;
+                    cur ^= 1;
+                    --t;
+                    last_exact = t;
+                    break;
+                }
+                if ((f_anchor - f) < P.stall_tol * f_anchor) {
+                    nsel = std::min(2 * nsel, nb);
+                    ++doublings;
+                    if (nsel >= nb) full = true;
+                }
+            }
+            ab ^= 1;
+            anchor_abs = tabs;
+            f_anchor = f;
+            ++anchors;
+            last_exact = t - 1;
+            continue;
+        }
+        const int steps = std::min(anchor_abs + E - tabs, P.max_iters - t);
         lists.assign((size_t)steps * nsel, 0);
-        for (int s = 0; s < steps; ++s) sample_blocks(P.seed, t + s, nb, nsel, perm, &lists[(size_t)s * nsel]);
+        for (int s2 = 0; s2 < steps; ++s2)
+            sample_blocks(P.seed, tabs + s2, nb, nsel, perm, &lists[(size_t)s2 * nsel]);
         HIPCHK(hipMemcpyAsync(L.blocks, lists.data(), sizeof(int) * lists.size(), hipMemcpyHostToDevice, st));
         HIPCHK(hipStreamSynchronize(st));
-        for (int s = 0; s < steps; ++s) {
-            rc = sampled_step(L.blocks + (size_t)s * nsel);
+        for (int s2 = 0; s2 < steps; ++s2) {
+            rc = sampled_step(L.blocks + (size_t)s2 * nsel);
             if (rc) return rc;
         }
     }
     // ---- full-batch branch (P2 sketch: g = 4 (H (H^T H) - S H))
-    if (full) {
+    if (full && !anchor_stop) {
         const int t0 = t, cur0 = cur;
         const int every = std::max(1, P.check_every);
         while (t < P.max_iters) {
             const int batch = std::min(every, P.max_iters - t);
             for (int b = 0; b < batch; ++b) {
-                rc = exact_step(false, 1 | 2 | 4);
+                rc = exact_step(-1, 1 | 2 | 4);
                 if (rc) return rc;
             }
             if ((rc = read_state())) return rc;
@@ -1143,17 +1225,18 @@ int symnmf_fit(const float* S, int64_t n, int64_t lds, int32_t k, const symnmf_f
         }
         if (stopped) {
             if (hd.status == -4) return SYMNMF_E_NONFINITE;
+            // launches after the stop step returned at once: not timings
+            prof_discard(call_tag | (hd.stop_iter + 1), call_tag | 0xFFFFFFFFll);
             t = hd.stop_iter;
-            cur_at_stop = (cur0 + (t - t0)) & 1;
-            cur = cur_at_stop;
+            cur = (cur0 + (t - t0)) & 1;
             last_exact = t;
         } else if (t > t0) {
             last_exact = t - 1;
         }
-    } else if ((rc = read_state())) {
-        return rc;
+    } else if (!anchor_stop) {
+        if ((rc = read_state())) return rc;
     }
-    const bool converged = stopped && hd.status == 1;
+    const bool converged = (stopped && hd.status == 1) || anchor_stop;
     const int iters = t;
 
     // ---- outputs
@@ -1170,8 +1253,30 @@ int symnmf_fit(const float* S, int64_t n, int64_t lds, int32_t k, const symnmf_f
     double f_last = std::nan("");
     if (last_exact >= 0)
         HIPCHK(hipMemcpyAsync(&f_last, L.f_trace + last_exact, sizeof(double), hipMemcpyDeviceToHost, st));
+    // the objective of the step before the returned H (NaN after a sampled
+    // step), for the state
+    double f_before = std::nan("");
+    if (iters >= 1)
+        HIPCHK(hipMemcpyAsync(&f_before, L.f_trace + iters - 1, sizeof(double), hipMemcpyDeviceToHost, st));
+    if (state && anchor_abs >= 0) {
+        HIPCHK(launch_copy(state->H_anchor, L.Ha[ab], nk, st));
+        HIPCHK(launch_copy(state->P_anchor, L.Pa[ab], nk, st));
+    }
     HIPCHK(hipStreamSynchronize(st));
 
+    if (state) {
+        state->iter = T0 + iters;
+        state->blocks = nsel;
+        state->anchor_iter = anchor_abs;
+        state->f_anchor = anchor_abs >= 0 ? f_anchor : std::nan("");
+        if (iters >= 1) {
+            state->f_prev_valid = std::isfinite(f_before) ? 1 : 0;
+            state->f_prev = f_before;
+        } else if (!restore) {
+            state->f_prev_valid = 0;
+            state->f_prev = std::nan("");
+        }  // no step taken after a restore: the entry values stand
+    }
     if (rep_host) {
         symnmf_fit_report& r = *rep_host;
         std::memset(&r, 0, sizeof(r));

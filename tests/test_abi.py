@@ -39,7 +39,7 @@ def test_every_declared_symbol_is_exported():
 
 def test_abi_version_and_status_strings():
     lib = L.load()
-    assert lib.symnmf_abi_version() == 4
+    assert lib.symnmf_abi_version() == 5
     for s in (0, 1, -1, -2, -3, -4, -5):
         assert len(L.status_string(s)) > 0
     assert L.status_string(12345) == "unknown status"
@@ -178,9 +178,10 @@ def test_fit_argument_validation():
     z = ctypes.c_size_t(1 << 40)
     rep = L.FitReport()
 
-    def call(params, n=100, lds=100, k=4, eig=None, n_eig=0, H=FAKE, G=None, ws=FAKE, wsb=z):
+    def call(params, n=100, lds=100, k=4, eig=None, n_eig=0, H=FAKE, G=None, ws=FAKE, wsb=z,
+             state=None):
         return lib.symnmf_fit(FAKE, n, lds, k, ctypes.byref(params), eig, n_eig, H, G, None, 0,
-                              ctypes.byref(rep), ws, wsb, None)
+                              ctypes.byref(rep), state, ws, wsb, None)
 
     def P(**kw):
         p = L.FitParams()
@@ -210,6 +211,28 @@ def test_fit_argument_validation():
     assert call(P(**full), ws=None) == L.E_WORKSPACE
     assert call(P(**full), wsb=ctypes.c_size_t(1024)) == L.E_WORKSPACE
     assert call(P(**full), ws=ctypes.c_void_p(0x10010)) == L.E_WORKSPACE  # misaligned
+    # the stop test's floor and the absolute step index
+    assert call(P(obj_floor=-1.0, **full)) == L.E_INVALID
+    assert call(P(obj_floor=float("nan"), **full)) == L.E_INVALID
+    assert call(P(start_iter=-1, **full)) == L.E_INVALID
+    assert call(P(start_iter=2 ** 31 - 10, max_iters=2000, **full)) == L.E_INVALID
+    # a state needs both anchor buffers; a restored one must match start_iter
+    # and hold a valid |B| and anchor
+    st = L.FitState()
+    st.iter, st.blocks, st.anchor_iter = 0, 1, -1
+    assert call(P(**full), state=ctypes.byref(st)) == L.E_INVALID        # no anchor buffers
+    st.H_anchor, st.P_anchor = FAKE.value, FAKE.value
+    res = dict(G=FAKE, state=ctypes.byref(st))
+    assert call(P(resume=1, start_iter=5, **full), **res) == L.E_INVALID   # iter != start_iter
+    st.iter = 5
+    st.blocks = 0
+    assert call(P(resume=1, start_iter=5, **full), **res) == L.E_INVALID   # |B| < 1
+    st.blocks = 99
+    assert call(P(resume=1, start_iter=5, block_rows=10, **full), **res) == L.E_INVALID  # |B| > nb
+    st.blocks, st.anchor_iter = 2, 6
+    assert call(P(resume=1, start_iter=5, block_rows=10, **full), **res) == L.E_INVALID  # future anchor
+    st.anchor_iter, st.f_anchor = 3, float("nan")
+    assert call(P(resume=1, start_iter=5, block_rows=10, **full), **res) == L.E_INVALID  # no f~
 
 
 def test_rms_decay_validated():
@@ -221,4 +244,4 @@ def test_rms_decay_validated():
         p.rms_decay = bad
         rep = L.FitReport()
         assert lib.symnmf_fit(FAKE, 100, 100, 4, ctypes.byref(p), None, 0, FAKE, None, None, 0,
-                              ctypes.byref(rep), FAKE, z, None) == L.E_INVALID
+                              ctypes.byref(rep), None, FAKE, z, None) == L.E_INVALID

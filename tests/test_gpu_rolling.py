@@ -87,20 +87,18 @@ def test_rolling_small_tpdm_links_match_oracle(small):
 
     A warm start sits near a stationary point, and AdaGrad's first step moves
     every coordinate by lr sign(g) (G starts at 0), so where many gradients are
-    at rounding level fp32 and fp64 take different signs and the two
-    trajectories part (several correct results). What is unique is compared:
-    the first step on every coordinate whose gradient is decided
-    (|g| > 1e-3 max|g|), and the whole 100-step objective trajectory (1e-3) on
-    links where fewer than 5% of the coordinates are undecided. On the other
-    links the outcome must be valid and comparable: H >= 0, the objective
-    falls, ends within 5% of the oracle's, labels agree (ARI >= 0.9). The
-    driver's own TPDM chain is checked for its block means."""
+    at rounding level fp32 and fp64 take different signs (several correct
+    first steps). What is unique is compared: the first step on every
+    coordinate whose gradient is decided (|g| > 1e-3 max|g|); then, from the
+    device's own state after that step (H_1 and G_1), the oracle's remaining
+    99 steps against the device's, on every link: objective trajectory within
+    1e-3 (of max(f, 1e-6 ||S||^2)) and labels ARI >= 0.99. The driver's own
+    TPDM chain is checked for its block means."""
     torch = require_gpu()
     from symmetric_nmf_clustering_amd import api
     st, S_win, res = small
     k = SMALL["k"]
     H_prev = None
-    strict = 0
     for t in range(W_SMALL):
         S = S_win["tpdm"][t].astype(np.float64)
         m = S.mean()
@@ -110,28 +108,27 @@ def test_rolling_small_tpdm_links_match_oracle(small):
         Sd, H0d = S_to_dev(S_win["tpdm"][t], torch), to_dev(H0, torch)
         # the first step on decided coordinates
         ref1 = oracle.fit_full(S, H0, lr, 1)
-        one = api.fit(Sd, k, solver="full", max_iters=1, tol_rel=0.0, H0=H0d).H.cpu().numpy()
+        first = api.fit(Sd, k, solver="full", max_iters=1, tol_rel=0.0, H0=H0d, return_G=True)
+        one = first.H.cpu().numpy()
         g = oracle.gradient(S, H0)
         decided = np.abs(g) > 1e-3 * np.abs(g).max()
         assert np.abs(one - ref1["H"])[decided].max() <= 1e-4 * lr, t
         assert one.min() >= 0.0 and np.abs(one - H0).max() <= lr * (1 + 1e-5), t
-        # 100 steps
-        ref = oracle.fit_full(S, H0, lr, ITERS)
+        # the remaining steps from the device's state after the first one
+        ref = oracle.fit_full(S, one.astype(np.float64), lr, ITERS - 1,
+                              G0=first.G.cpu().numpy().astype(np.float64))
         got = api.fit(Sd, k, solver="full", max_iters=ITERS, tol_rel=0.0, H0=H0d)
         s2 = float((S * S).sum())
-        fg, fr = got.f_trace, np.asarray(ref["f"])
+        fg, fr = got.f_trace[1:], np.asarray(ref["f"])
         Hg = got.H.cpu().numpy()
-        assert Hg.min() >= 0.0 and fg[-1] < fg[0], t
-        if np.mean(~decided) < 0.05:
-            strict += 1
-            assert np.all(np.abs(fg - fr) <= 1e-3 * np.maximum(np.abs(fr), 1e-6 * s2)), t
-        else:
-            assert abs(fg[-1] - fr[-1]) <= 0.05 * fr[-1], (t, fg[-1], fr[-1])
-            assert adjusted_rand_score(Hg.argmax(axis=1), oracle.labels(ref["H"])) >= 0.9, t
+        assert Hg.min() >= 0.0, t
+        rel = np.abs(fg - fr) / np.maximum(np.abs(fr), 1e-6 * s2)
+        assert rel.max() <= 1e-3, (t, float(rel.max()), int(rel.argmax()))
+        ari = adjusted_rand_score(Hg.argmax(axis=1), oracle.labels(ref["H"]))
+        assert ari >= 0.99, (t, ari)
         H_prev = ref["H"]
         B = oracle.cross_block_means(S, st.labels_after, st.stress_groups)
         np.testing.assert_allclose(res["kinds"]["tpdm"]["block_means"][t], B, rtol=1e-5)
-    assert strict >= 10
 
 
 def test_rolling_small_cold_start_is_per_window_seeded_fit():
