@@ -51,7 +51,8 @@ enum symnmf_status {
     SYMNMF_E_WORKSPACE = -2,    /* workspace missing, misaligned or too small */
     SYMNMF_E_HIP = -3,          /* a HIP runtime call failed */
     SYMNMF_E_NONFINITE = -4,    /* NaN/Inf in the input or in the objective */
-    SYMNMF_E_DEGENERATE = -5    /* a constant column (correlation undefined) */
+    SYMNMF_E_DEGENERATE = -5,   /* a constant column (correlation undefined) */
+    SYMNMF_E_TOO_LARGE = -6     /* beyond symnmf_sh_noalloc's static scratch    */
 };
 
 /* Dependence matrix kinds (P1 introduction; P3). */
@@ -220,6 +221,23 @@ int symnmf_spectral_probe(const float* S, int64_t n, int64_t lds, int32_t p,
  * a direct-to-LDS ring); the result is bit for bit the same either way. */
 int symnmf_sh(const float* S, int64_t n, int64_t lds, const float* H, int32_t k,
               float* P, double* tr_host, void* ws, size_t ws_bytes, void* hip_stream);
+
+/* symnmf_sh for callers that cannot allocate device memory (code under HIP
+ * graph capture, tight serving loops, harnesses that forbid allocation). Same
+ * product with the same kernels, so P and the trace are bit for bit those of
+ * symnmf_sh: P = S H (n x k, ld k) and, if tr is non-null, *tr = tr(H^T S H)
+ * written on the DEVICE (one double, 8-byte aligned). No workspace argument:
+ * the scratch is a static device array of 64 MiB that each device the library
+ * runs on holds until the process ends. A problem whose symnmf_sh workspace
+ * (symnmf_workspace_bytes(SYMNMF_OP_SH, n, k, 0, NULL)) exceeds 64 MiB is
+ * rejected with SYMNMF_E_TOO_LARGE before any device work (n up to ~21 800 at
+ * k = 24). Asynchronous on hip_stream; the call allocates nothing and never
+ * synchronises. Every call on a device shares that device's scratch, so calls
+ * that overlap on one device (other streams, other threads) race; serialise
+ * them. Requires 1 <= k <= 128, lds >= n, lds % 4 == 0, S 16-byte aligned.
+ * Errors: E_INVALID, E_TOO_LARGE, E_HIP. */
+int symnmf_sh_noalloc(const float* S, int64_t n, int64_t lds, const float* H, int32_t k,
+                      float* P, double* tr, void* hip_stream);
 
 /* The S.H pass from the upper triangle (P1 "Factorization at scale": the
  * S H products dominate; P1 introduction: S, an absolute correlation or a

@@ -19,6 +19,7 @@ E_WORKSPACE = -2
 E_HIP = -3
 E_NONFINITE = -4
 E_DEGENERATE = -5
+E_TOO_LARGE = -6
 
 ABSCORR, TPDM = 0, 1
 AUTO, FULL, BLOCK_SVRG = 0, 1, 2
@@ -115,6 +116,7 @@ SIGNATURES = [
       ctypes.POINTER(_I32), _P, ctypes.c_size_t, _P]),
     ("symnmf_sh", ctypes.c_int,
      [_P, _I64, _I64, _P, _I32, _P, ctypes.POINTER(_D), _P, ctypes.c_size_t, _P]),
+    ("symnmf_sh_noalloc", ctypes.c_int, [_P, _I64, _I64, _P, _I32, _P, _P, _P]),
     ("symnmf_sh_sym", ctypes.c_int,
      [_P, _I64, _I64, _P, _I32, _P, ctypes.POINTER(_D), _P, ctypes.c_size_t, _P]),
     ("symnmf_sq", ctypes.c_int,

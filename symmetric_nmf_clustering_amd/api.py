@@ -129,6 +129,24 @@ def sh(S: torch.Tensor, H: torch.Tensor):
     return P, tr.value
 
 
+def sh_noalloc(S: torch.Tensor, H: torch.Tensor, out: Optional[torch.Tensor] = None,
+               tr_out: Optional[torch.Tensor] = None):
+    """The S.H pass on the library's static scratch (no workspace, no device
+    allocation inside the call): returns (P, tr) with tr a one-element float64
+    device tensor. ``out`` and ``tr_out`` let the caller own every buffer."""
+    n, lds = _S_layout(S)
+    _require_cuda(H, "H")
+    if H.dim() != 2 or H.shape[0] != n or not H.is_contiguous():
+        raise ValueError("H must be a contiguous n x k tensor")
+    k = H.shape[1]
+    P = torch.empty_like(H) if out is None else out
+    tr = torch.empty(1, dtype=torch.float64, device=S.device) if tr_out is None else tr_out
+    st = L.load().symnmf_sh_noalloc(_ptr(S), n, lds, _ptr(H), k, _ptr(P), _ptr(tr),
+                                    ctypes.c_void_p(_stream_ptr()))
+    L.check(st, "symnmf_sh_noalloc")
+    return P, tr
+
+
 def sh_sym(S: torch.Tensor, H: torch.Tensor):
     """The S.H pass from the upper triangle of a symmetric S (each block on or
     above the diagonal read once, bf16 matrix cores with split operands):

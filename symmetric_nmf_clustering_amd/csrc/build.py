@@ -15,7 +15,7 @@ ROOT = os.path.dirname(PKG)
 OUT_DIR = os.path.join(PKG, "lib")
 OUT = os.path.join(OUT_DIR, "libsymnmf.so")
 SOURCES = ["symnmf.cpp", "k_sh.hip", "k_fit.hip", "k_build.hip", "k_kmeans.hip", "k_sq.hip",
-           "k_sym.hip"]
+           "k_sym.hip", "noalloc.hip"]
 
 FLAGS = [
     "--offload-arch=gfx950",

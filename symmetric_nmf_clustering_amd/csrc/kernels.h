@@ -59,6 +59,13 @@ struct FitDev {
 // rows of the plan are read from X.
 hipError_t launch_sh_panel(const float* S, int64_t lds, const float* X, int width,
                            const RowPlan& rp, int nsplit, float* part, int ldp, hipStream_t st);
+// Rows per split of a full pass: at most kMaxSplits splits of at least 64 rows
+// (a multiple of 4), so one output accumulates at most ceil(n / kMaxSplits)
+// rows in fp32 before the fixed-order split sum. Every split is non-empty.
+inline int sh_full_rows_per_split(int n) {
+    const int per = (n + kMaxSplits - 1) / kMaxSplits;
+    return ((per > 64 ? per : 64) + 3) / 4 * 4;
+}
 // ---- the probe's S.Q pass on the bf16 matrix cores (k_sq.hip) -------------
 // Q is packed once per pass into the matrix core's B operands (each fp32 value
 // split exactly into three bf16 parts); the pass then writes

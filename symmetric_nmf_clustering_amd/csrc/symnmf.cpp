@@ -152,9 +152,7 @@ struct FullPlan {
     int nsplit;
 };
 FullPlan full_plan(int n) {
-    // at most kMaxSplits splits, at least 64 rows each: one output accumulates
-    // at most ceil(n / kMaxSplits) rows in fp32 before the fixed-order split sum
-    int rps = (int)round_up(std::max<int64_t>(64, cdiv(n, kMaxSplits)), 4);
+    const int rps = sh_full_rows_per_split(n);
     FullPlan fp;
     fp.nsplit = (int)cdiv(n, rps);
     fp.rp = RowPlan{n, rps, nullptr, 0, 0, 1, 0, 1};
@@ -550,6 +548,8 @@ const char* symnmf_status_string(int status) {
         case SYMNMF_E_HIP: return "HIP runtime error";
         case SYMNMF_E_NONFINITE: return "non-finite value in input or objective";
         case SYMNMF_E_DEGENERATE: return "constant column: correlation undefined";
+        case SYMNMF_E_TOO_LARGE:
+            return "problem too large for the 64 MiB static scratch of symnmf_sh_noalloc";
         default: return "unknown status";
     }
 }

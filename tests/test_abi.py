@@ -40,8 +40,8 @@ def test_every_declared_symbol_is_exported():
 def test_abi_version_and_status_strings():
     lib = L.load()
     assert lib.symnmf_abi_version() == 5
-    for s in (0, 1, -1, -2, -3, -4, -5):
-        assert len(L.status_string(s)) > 0
+    for s in (0, 1, -1, -2, -3, -4, -5, -6):
+        assert L.status_string(s) != "unknown status"
     assert L.status_string(12345) == "unknown status"
 
 
@@ -64,7 +64,8 @@ def test_struct_layout_matches_the_c_compiler(tmp_path):
     if cc is None:
         pytest.skip("no C compiler")
     lines = ['#include <stdio.h>', '#include <stddef.h>', '#include "symnmf.h"', 'int main(void) {']
-    for cname, cls in (("symnmf_fit_params", L.FitParams), ("symnmf_fit_report", L.FitReport)):
+    for cname, cls in (("symnmf_fit_params", L.FitParams), ("symnmf_fit_report", L.FitReport),
+                       ("symnmf_fit_state", L.FitState)):
         lines.append(f'printf("{cname} size %zu\\n", sizeof({cname}));')
         for f, _ in cls._fields_:
             lines.append(f'printf("{cname} {f} %zu\\n", offsetof({cname}, {f}));')
@@ -75,7 +76,8 @@ def test_struct_layout_matches_the_c_compiler(tmp_path):
     subprocess.run([cc, "-I", os.path.join(ROOT, "include"), str(src), "-o", str(exe)], check=True)
     out = subprocess.run([str(exe)], check=True, capture_output=True, text=True).stdout.split("\n")
     got = {(a, b): int(c) for a, b, c in (l.split() for l in out if l.strip())}
-    for cname, cls in (("symnmf_fit_params", L.FitParams), ("symnmf_fit_report", L.FitReport)):
+    for cname, cls in (("symnmf_fit_params", L.FitParams), ("symnmf_fit_report", L.FitReport),
+                       ("symnmf_fit_state", L.FitState)):
         assert got[(cname, "size")] == ctypes.sizeof(cls)
         for f, _ in cls._fields_:
             assert got[(cname, f)] == getattr(cls, f).offset, (cname, f)
@@ -245,3 +247,25 @@ def test_rms_decay_validated():
         rep = L.FitReport()
         assert lib.symnmf_fit(FAKE, 100, 100, 4, ctypes.byref(p), None, 0, FAKE, None, None, 0,
                               ctypes.byref(rep), None, FAKE, z, None) == L.E_INVALID
+
+
+def test_sh_noalloc_rejects_before_any_device_work():
+    """The no-allocation S.H pass validates its arguments and its size limit
+    (the symnmf_sh workspace must fit the 64 MiB static scratch) on the host
+    and returns before touching the device."""
+    lib = L.load()
+    f = lib.symnmf_sh_noalloc
+    tr = ctypes.c_void_p(0x100008)
+    assert f(None, 100, 100, FAKE, 4, FAKE, None, None) == L.E_INVALID
+    assert f(FAKE, 100, 100, None, 4, FAKE, None, None) == L.E_INVALID
+    assert f(FAKE, 100, 100, FAKE, 0, FAKE, None, None) == L.E_INVALID
+    assert f(FAKE, 100, 100, FAKE, 129, FAKE, None, None) == L.E_INVALID
+    assert f(FAKE, 100, 98, FAKE, 4, FAKE, None, None) == L.E_INVALID       # lds < n
+    assert f(FAKE, 100, 102, FAKE, 4, FAKE, None, None) == L.E_INVALID      # lds % 4
+    assert f(ctypes.c_void_p(0x10004), 100, 100, FAKE, 4, FAKE, None, None) == L.E_INVALID
+    assert f(FAKE, 100, 100, FAKE, 4, FAKE, ctypes.c_void_p(0x100004), None) == L.E_INVALID
+    limit = 64 << 20
+    for n, k in ((22000, 24), (100000, 24), (8192, 128), (30000, 17)):
+        assert lib.symnmf_workspace_bytes(L.OP_SH, n, k, 0, None) > limit
+        assert f(FAKE, n, n + (-n) % 4, FAKE, k, FAKE, tr, None) == L.E_TOO_LARGE, (n, k)
+    assert "64 MiB" in L.status_string(L.E_TOO_LARGE)
