@@ -53,6 +53,8 @@ def parse():
                     help="CPU time the oracle baseline spends on its timed sample")
     ap.add_argument("--seeds", type=int, default=3,
                     help="seeds of the untimed time-to-convergence sweep (|corr| and TPDM); 0 skips it")
+    ap.add_argument("--no-cold-warm", action="store_true",
+                    help="skip the untimed cold/warm-start comparison on the next day's window")
     return ap.parse_args()
 
 
@@ -103,6 +105,45 @@ def cpu_baseline(w, k, rows, seconds=10.0):
                        f"{reps_sh} repetitions, {reps_sh * t_sh:.1f} s) plus the full n x k "
                        f"gradient/AdaGrad update ({reps_rest} repetitions, {reps_rest * t_rest:.1f} s)"),
             "seconds_per_iter": per_iter}
+
+
+def cold_warm(args, w, X, S, res_t, api, synth, metrics, sh_pass):
+    """Untimed: the window one day on (the same returns moved by a day, one new
+    day of the recipe), fitted cold (the pages' protocol: the same seeded
+    initialisation for every window) and warm (from the timed jobs' H of the
+    current window, fresh accumulator), both with AdaptGrow from that window's
+    probe, to convergence."""
+    import numpy as np
+    import torch
+    nxt = synth.student_factor_next(n=w.n, k=w.k, T=w.T, seed=w.seed, shift=1)
+    X.copy_(torch.from_numpy(nxt.X))
+    api.build_S(X, "abscorr", out=S)
+    ev, pits, _ = api.spectral_probe(S, p=args.probe_p, max_iters=args.probe_iters, tol=1e-6,
+                                     seed=0)
+    out = {"window": "the timed window moved by one day (student_factor_next, shift 1)",
+           "probe_iters": pits}
+    H_t = res_t.H.clone()
+    labels = {}
+    for name, kw in (("cold", {}), ("warm", {"H0": H_t})):
+        torch.cuda.synchronize()
+        t = time.perf_counter()
+        r = api.fit(S, w.k, solver=args.solver, eigvals=ev, max_iters=args.max_iters,
+                    tol_rel=1e-6, seed=0, sh_pass=sh_pass, **kw)
+        torch.cuda.synchronize()
+        dt = time.perf_counter() - t
+        lab = api.labels(r.H).cpu().numpy()
+        labels[name] = lab
+        rep = r.report
+        out[name] = {"fit_s": dt, "fit_iterations": rep["iterations"],
+                     "converged": bool(rep["converged"]),
+                     "start_branch": "full" if rep["start_branch"] == 0 else "block_svrg",
+                     "doublings": rep["doublings"], "f_last": rep["f_last"],
+                     "ari_vs_planted": metrics.adjusted_rand_index(lab, w.labels)}
+        print(f"[bench] next window {name}: {rep['iterations']} it in {dt:.2f} s, "
+              f"converged={rep['converged']}", file=sys.stderr, flush=True)
+    out["ari_cold_vs_warm"] = metrics.adjusted_rand_index(labels["cold"], labels["warm"])
+    X.copy_(torch.from_numpy(w.X))
+    return out
 
 
 def measured_traffic(name):
@@ -306,6 +347,8 @@ def main():
                            "probe_plus_fit_s_mean": float(np.mean([r["fit_s"] + r["probe_ms"] / 1e3
                                                                    for r in runs]))}
         out["seeds"] = sweep
+    if not args.no_cold_warm:
+        out["cold_warm"] = cold_warm(args, w, X, S, res, api, synth, metrics, sh_pass)
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(w, k, args.cpu_rows, args.cpu_seconds)
     print(json.dumps(out), flush=True)

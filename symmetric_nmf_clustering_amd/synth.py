@@ -111,6 +111,33 @@ def student_factor(n: int = 8192, k: int = 24, T: int = 252, seed: int = 1,
                   {"sizes": sizes.tolist()})
 
 
+def student_factor_next(n: int = 8192, k: int = 24, T: int = 252, seed: int = 1,
+                        shift: int = 1, min_size: int = 64) -> Window:
+    """The ``student_factor`` window moved ``shift`` days on: days shift ..
+    T - 1 of ``student_factor(n, k, T, seed)`` followed by ``shift`` new days of
+    the same recipe (same groups and loadings), for warm-start comparisons
+    between consecutive windows.
+
+    Draw order: ``student_factor``'s draws (to recover the groups and
+    loadings), then from ``default_rng([seed, 2])``, day by day, the new day's
+    factors (k) and noise (n), so the days after the window do not depend on
+    ``shift``.
+    """
+    base = student_factor(n, k, T, seed, min_size)
+    rng0 = np.random.default_rng(seed)
+    _student_groups(rng0, n, k, min_size)
+    load = rng0.uniform(0.3, 0.9, size=n)
+    rng = np.random.default_rng([seed, 2])
+    new = np.empty((shift, n))
+    for d in range(shift):
+        f = _t4_unit(rng, k)
+        e = _t4_unit(rng, n)
+        new[d] = load * f[base.labels] + np.sqrt(1.0 - load * load) * e
+    X = np.concatenate([base.X[shift:].astype(np.float64), new], axis=0)
+    return Window(np.ascontiguousarray(X, dtype=np.float32), base.labels, k, "student_factor_next",
+                  seed, {"sizes": base.meta["sizes"], "shift": shift})
+
+
 def student_factor_stress(n: int = 8192, k: int = 24, T: int = 252,
                           seed: int = 1, min_size: int = 64,
                           stress_groups: int = 4, stress_days: int = 10,

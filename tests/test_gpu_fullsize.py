@@ -288,3 +288,54 @@ def test_fullsize_spherical_kmeans(big):
     assert np.all(sims[np.arange(rows.size), lab[rows]] >= best - 1e-5 * np.abs(best))
     # a local optimum from k seeded random rows (measured ARI 0.89)
     assert adjusted_rand_score(lab, w.labels) >= 0.8
+
+
+def test_fullsize_warm_start_next_window(big):
+    """Cold vs warm start at full size: the window one day on (the returns moved
+    by a day plus one new day of the recipe), fitted from the current window's
+    H with a fresh accumulator, as Block-SVRG starts here (32 of 98 blocks).
+    Its first two steps on sampled rows against the oracle, which builds those
+    rows of the new S from the shifted returns: the anchor step (exact S' H),
+    then, from the device's state after it, the sampled step (the anchor's
+    product plus 98/32 times the sampled blocks' correction). Compared where
+    the gradient is decided well above fp32 noise, as the cold-start tests."""
+    torch, api, w, S, fro, rows = big
+    lr_b, phi0, seed = 0.05, 32.0 / 98.0, 5
+    base = api.fit(S, K, solver="full", init="uniform", init_scale=0.1, seed=0, lr=lr_b,
+                   max_iters=100, tol_rel=0.0, sh_pass="upper")
+    Ht = base.H
+    nxt = synth.student_factor_next(n=N, k=K, T=w.T, seed=w.seed, shift=1)
+    S2, _ = api.build_S(to_dev(nxt.X, torch), "abscorr")
+    kw = dict(solver="block_svrg", phi0=phi0, seed=seed, tol_rel=0.0, sh_pass="upper", H0=Ht,
+              return_G=True)
+    one = api.fit(S2, K, max_iters=1, **kw)
+    two = api.fit(S2, K, max_iters=2, **kw)
+    del S2
+    assert one.report["blocks_final"] == 32 and one.report["anchors"] == 1
+    lr, eps = one.report["lr_used"], 1e-8
+    H0 = Ht.cpu().numpy().astype(np.float64)
+    S_rows = oracle.abs_corr_rows(nxt.X, rows)          # rows of the new S, fp64
+    P0, _ = oracle.sh_product(S_rows, H0, rows=rows)
+    g0 = 4.0 * (H0[rows] @ (H0.T @ H0) - P0)
+    H1_ref = np.maximum(H0[rows] - lr * g0 / (np.abs(g0) + eps), 0.0)
+    dec0 = np.abs(g0) > 1e-3 * np.abs(g0).max()
+    assert dec0.mean() > 0.8, dec0.mean()
+    H1 = one.H.cpu().numpy().astype(np.float64)
+    err1 = np.abs(H1[rows] - H1_ref)[dec0].max()
+    # the sampled step from the device's (H1, G1): the correction of row i is
+    # sum over the sampled blocks' rows j of S'[i, j] (H1 - H0)[j]
+    G1 = one.G.cpu().numpy().astype(np.float64)
+    blocks = oracle.sample_blocks(seed, 1, 98, 32)
+    cols = np.concatenate([np.arange(b * 1024, min(N, (b + 1) * 1024)) for b in blocks])
+    corr = S_rows[:, cols] @ (H1[cols] - H0[cols])
+    P1 = P0 + (98.0 / 32.0) * corr
+    g1 = 4.0 * (H1[rows] @ (H1.T @ H1) - P1)
+    G2 = G1[rows] + g1 * g1
+    H2_ref = np.maximum(H1[rows] - lr * g1 / (np.sqrt(G2) + eps), 0.0)
+    dec1 = np.abs(g1) > 1e-3 * np.abs(g1).max()
+    H2 = two.H.cpu().numpy().astype(np.float64)[rows]
+    err2 = np.abs(H2 - H2_ref)[dec1].max()
+    print(f"warm start, next window: first step {err1:.2e}, sampled step {err2:.2e} "
+          f"(decided {dec0.mean():.3f} / {dec1.mean():.3f})")
+    assert err1 <= 1e-5 and err2 <= 1e-5, (err1, err2)
+    assert np.isnan(two.f_trace[1]) and np.isfinite(two.f_trace[0])

@@ -113,3 +113,19 @@ def test_tpdm_rows_consistent():
     w = synth.student_factor_stress(n=200, k=4, T=60, seed=2, min_size=20)
     rows = [3, 0, 199]
     np.testing.assert_allclose(oracle.tpdm_rows(w.X, rows), oracle.tpdm(w.X)[rows], atol=1e-15)
+
+
+def test_shifted_window_continues_the_stream():
+    """student_factor_next: the window one day on shares T - 1 days with the
+    original window, keeps its groups, and adds a day of the same recipe."""
+    from symmetric_nmf_clustering_amd import synth
+    a = synth.student_factor(n=600, k=6, T=50, seed=4, min_size=20)
+    b = synth.student_factor_next(n=600, k=6, T=50, seed=4, shift=1, min_size=20)
+    c = synth.student_factor_next(n=600, k=6, T=50, seed=4, shift=3, min_size=20)
+    assert b.X.shape == a.X.shape and np.array_equal(b.X[:-1], a.X[1:])
+    assert np.array_equal(c.X[:-3], a.X[3:]) and np.array_equal(c.X[-3], b.X[-1])
+    assert np.array_equal(b.labels, a.labels)
+    # the new day carries the planted groups: members of a group co-move
+    S_new = oracle.abs_corr(np.vstack([a.X, c.X[-3:]]))
+    same = b.labels[:, None] == b.labels[None, :]
+    assert S_new[same].mean() > 3 * S_new[~same].mean()
