@@ -29,11 +29,17 @@
 //    columns c0 + 16g + 8h + e for half h; H's rows are packed in that map
 //    ("row map"), once per pass.
 //
+// The row-side products run as D^T = H^T (factor x column) times the parts
+// (column x row), so a lane ends with four consecutive factors of one row: the
+// per-panel sum over the eight waves is then one float2 per thread and one
+// store per thread (see reduce_rows).
+//
 // Work: strips of 512 columns (8 waves), each walked down in chunks of 4096
 // rows. Workgroup (strip s, chunk qc) covers rows [4096 qc, min(4096 (qc+1),
 // E_s)), E_s = min(n, 512 (s + 1)): the part of the strip on or above the
 // diagonal. Per 32-row panel the eight waves' row-side sums meet in LDS and
-// leave as one partial P1[s][i] per (strip, row); the column side accumulates
+// leave as one partial P1[s][i] per (strip, row; rows of p1_ld(k) floats);
+// the column side accumulates
 // in registers over the chunk and leaves as P2[qc][s][j] per (chunk, column).
 // The fold adds, for row i of strip s(i) = i / 512,
 //     sum over s = s(i) .. NS-1 of P1[s][i], then
@@ -54,6 +60,10 @@ constexpr int kSymWaves = kSymStrip / 64;  // waves per workgroup, 64 columns ea
 __host__ __device__ inline int64_t p1_rows_before(int s) {
     return (int64_t)(kSymStrip / 2) * s * (s + 1);
 }
+// row pitch of P1: the row-side sums are stored as float2 pairs of factors
+__host__ __device__ inline int p1_ld(int k) { return (k + 3) / 4 * 4; }
+// floats of the store sink after P1 (one float2 per thread of a workgroup)
+constexpr int kSymSinkFloats = 2 * 64 * kSymWaves;
 
 // (a, b) -> the bf16 pair of two fp32 values that are bf16-exact (their high
 // halves; a in the low half, as the matrix core reads a pair)
@@ -256,15 +266,17 @@ __global__ __launch_bounds__(64 * kSymWaves) void sym_kernel(
 #pragma unroll
                         for (int t = 0; t < NT; ++t) {
                             // the terms a_p b_r with p + r <= 4 (parts numbered 1..3)
+                            // as D^T: hj (H^T, factor x column) is the A
+                            // operand and the part (column x row) the B one
                             if (p == 2) {
-                                acc1[rho][t] = mfma_bf16(ap, hj[h][t][0], acc1[rho][t]);
+                                acc1[rho][t] = mfma_bf16(hj[h][t][0], ap, acc1[rho][t]);
                             } else if (p == 1) {
-                                acc1[rho][t] = mfma_bf16(ap, hj[h][t][1], acc1[rho][t]);
-                                acc1[rho][t] = mfma_bf16(ap, hj[h][t][0], acc1[rho][t]);
+                                acc1[rho][t] = mfma_bf16(hj[h][t][1], ap, acc1[rho][t]);
+                                acc1[rho][t] = mfma_bf16(hj[h][t][0], ap, acc1[rho][t]);
                             } else {
-                                acc1[rho][t] = mfma_bf16(ap, hj[h][t][2], acc1[rho][t]);
-                                acc1[rho][t] = mfma_bf16(ap, hj[h][t][1], acc1[rho][t]);
-                                acc1[rho][t] = mfma_bf16(ap, hj[h][t][0], acc1[rho][t]);
+                                acc1[rho][t] = mfma_bf16(hj[h][t][2], ap, acc1[rho][t]);
+                                acc1[rho][t] = mfma_bf16(hj[h][t][1], ap, acc1[rho][t]);
+                                acc1[rho][t] = mfma_bf16(hj[h][t][0], ap, acc1[rho][t]);
                             }
                         }
                     }
@@ -277,29 +289,32 @@ __global__ __launch_bounds__(64 * kSymWaves) void sym_kernel(
             for (int t = 0; t < NT; ++t) red[hb][wave][rho][t][lane] = acc1[rho][t];
     };
 
-    // the waves' row-side sums of panel a, in wave order, to P1
+    // The waves' row-side sums of panel a, in wave order, to P1. Lane
+    // (lr, g') of acc1[rho][t] holds factors 16 t + 4 g' .. +3 of row
+    // 32 a + 16 rho + lr, so thread h sums one float2 (half h & 1 of the
+    // float4 at h >> 1 of each wave's block) over the eight waves and stores
+    // it. Every thread stores exactly once (a thread without an output, or
+    // an output past n or past k, writes the sink): with no branch around
+    // the store, the compiler counts it exactly and never waits for it when
+    // it waits for the next panel's loads (a store in a branch made every
+    // panel wait for the previous panel's stores to complete).
+    const int ldp1 = p1_ld(k);
+    float* __restrict__ sink = P1 + (p1_rows_before(NS - 1) + n) * (int64_t)ldp1 + 2 * tid;
     auto reduce_rows = [&](int a) {
-        const float* rf = reinterpret_cast<const float*>(&red[a & 1][0][0][0][0]);
-        constexpr int WSTRIDE = 2 * NT * 64 * 4;  // floats per wave in red
-        // a fixed trip count, no loop: a loop here makes the compiler wait for
-        // every load in flight (the next panel's) before entering it
+        constexpr int HALVES = 4 * NT * 64;  // float2 outputs of a panel
+        static_assert(HALVES <= NTH, "one output per thread at most");
+        const int h = tid < HALVES ? tid : 0;
+        const f32x2* rq = reinterpret_cast<const f32x2*>(&red[a & 1][0][0][0][0]);
+        f32x2 sum = rq[h];
 #pragma unroll
-        for (int m = 0; m < (32 * 16 * NT + NTH - 1) / NTH; ++m) {
-            const int o = tid + NTH * m;
-            if (o >= 32 * k) break;
-            const int rr = o / k;
-            const int c = o - rr * k;
-            const int i = 32 * a + rr;
-            const int rho = rr >> 4;
-            const int gg = (rr >> 2) & 3;
-            const int r = rr & 3;
-            const int t = c >> 4;
-            const int idx = ((rho * NT + t) * 64 + 16 * gg + (c & 15)) * 4 + r;
-            float sum = rf[idx];
-#pragma unroll
-            for (int w = 1; w < WAVES; ++w) sum += rf[w * WSTRIDE + idx];
-            if (i < n) P1[(p1base + i) * k + c] = sum;
-        }
+        for (int w = 1; w < WAVES; ++w) sum += rq[w * HALVES + h];
+        const int o = h >> 1;
+        const int ln = o & 63, t = (o >> 6) % NT, rho = o / (64 * NT);
+        const int fq = 16 * t + 4 * (ln >> 4) + 2 * (h & 1);
+        const int i = 32 * a + 16 * rho + (ln & 15);
+        const bool ok = tid < HALVES && fq < k && i < n;
+        float* dstp = ok ? P1 + (p1base + i) * ldp1 + fq : sink;
+        *reinterpret_cast<f32x2*>(dstp) = sum;
     };
 
     // One panel: issue the next panel's packed H rows and S, multiply this
@@ -352,6 +367,7 @@ __global__ __launch_bounds__(256) void sym_fold_kernel(const float* __restrict__
                                                        const int* __restrict__ done) {
     if (done && *done) return;
     __shared__ double redd[4];
+    const int ldp1 = p1_ld(k);
     const int row0 = blockIdx.x * kUpdRows;
     const int rows = min(kUpdRows, n - row0);
     double acc = 0.0;
@@ -364,11 +380,11 @@ __global__ __launch_bounds__(256) void sym_fold_kernel(const float* __restrict__
         for (; sp + 8 <= NS; sp += 8) {
             float v[8];
 #pragma unroll
-            for (int u = 0; u < 8; ++u) v[u] = P1[(p1_rows_before(sp + u) + i) * k + c];
+            for (int u = 0; u < 8; ++u) v[u] = P1[(p1_rows_before(sp + u) + i) * ldp1 + c];
 #pragma unroll
             for (int u = 0; u < 8; ++u) sum += v[u];
         }
-        for (; sp < NS; ++sp) sum += P1[(p1_rows_before(sp) + i) * k + c];
+        for (; sp < NS; ++sp) sum += P1[(p1_rows_before(sp) + i) * ldp1 + c];
         const int nch = (min(n, kSymStrip * (si + 1)) + kSymChunk - 1) / kSymChunk;
         const int64_t qstride = (int64_t)NS * kSymStrip * k;
         sum += ordered_strided_sum(
@@ -389,7 +405,7 @@ SymPlan sym_plan(int n, int k) {
     p.nt = (k + 15) / 16;
     p.ns = (n + kSymStrip - 1) / kSymStrip;
     p.nq = (n + kSymChunk - 1) / kSymChunk;
-    p.p1_floats = (size_t)(p1_rows_before(p.ns - 1) + n) * k;
+    p.p1_floats = (size_t)(p1_rows_before(p.ns - 1) + n) * p1_ld(k) + kSymSinkFloats;
     p.p2_floats = (size_t)p.nq * p.ns * kSymStrip * k;
     p.nkb_col = (n + 31) / 32;
     p.nkb_row = 2 * ((n + 63) / 64);
