@@ -344,21 +344,24 @@ __global__ __launch_bounds__(64 * kSymWaves) void sym_kernel(
 
     // column side of the chunk: lane (lr, g') holds column c0 + 4 lr + q,
     // factor columns 16t + 4g' + r
-    float* __restrict__ dst = P2 + ((int64_t)qc * NS + s) * kSymStrip * k;
+    // (rows of p1_ld(k) floats: one float4 of four factors per store)
+    float* __restrict__ dst = P2 + ((int64_t)qc * NS + s) * kSymStrip * ldp1;
 #pragma unroll
     for (int q = 0; q < 4; ++q)
 #pragma unroll
-        for (int t = 0; t < NT; ++t)
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int c = 16 * t + 4 * g + r;
-                if (c < k) dst[(int64_t)(64 * wave + 4 * lr + q) * k + c] = acc2[q][t][r];
-            }
+        for (int t = 0; t < NT; ++t) {
+            const int c = 16 * t + 4 * g;
+            if (c < ldp1)
+                *reinterpret_cast<floatx4*>(dst + (int64_t)(64 * wave + 4 * lr + q) * ldp1 + c) =
+                    acc2[q][t];
+        }
 }
 
 // P[i][c] (ld ldP) = sum over s >= i / 512 of P1[s][i][c], then over the chunks of
 // strip i / 512 of P2[qc][s(i)][i][c]; tr_part[b] = sum over the rows of block
-// b of <Hdot_i, P_i> (fp64), blocks of kUpdRows rows.
+// b of <Hdot_i, P_i> (fp64), blocks of kUpdRows rows. A thread sums four
+// factors at once (float4 loads of the p1_ld(k)-float rows of P1 and P2), each
+// in the same order as a scalar sum would.
 __global__ __launch_bounds__(256) void sym_fold_kernel(const float* __restrict__ P1,
                                                        const float* __restrict__ P2, int n, int k,
                                                        int NS, float* __restrict__ P, int ldP,
@@ -368,29 +371,37 @@ __global__ __launch_bounds__(256) void sym_fold_kernel(const float* __restrict__
     if (done && *done) return;
     __shared__ double redd[4];
     const int ldp1 = p1_ld(k);
+    const int kq = ldp1 / 4;
     const int row0 = blockIdx.x * kUpdRows;
     const int rows = min(kUpdRows, n - row0);
     double acc = 0.0;
-    for (int e = threadIdx.x; e < rows * k; e += 256) {
-        const int i = row0 + e / k;
-        const int c = e % k;
+    for (int e = threadIdx.x; e < rows * kq; e += 256) {
+        const int i = row0 + e / kq;
+        const int c = 4 * (e % kq);
         const int si = i / kSymStrip;
-        float sum = 0.f;
+        floatx4 sum = {0.f, 0.f, 0.f, 0.f};
         int sp = si;
         for (; sp + 8 <= NS; sp += 8) {
-            float v[8];
+            floatx4 v[8];
 #pragma unroll
-            for (int u = 0; u < 8; ++u) v[u] = P1[(p1_rows_before(sp + u) + i) * ldp1 + c];
+            for (int u = 0; u < 8; ++u)
+                v[u] = *reinterpret_cast<const floatx4*>(P1 + (p1_rows_before(sp + u) + i) * ldp1 + c);
 #pragma unroll
             for (int u = 0; u < 8; ++u) sum += v[u];
         }
-        for (; sp < NS; ++sp) sum += P1[(p1_rows_before(sp) + i) * ldp1 + c];
+        for (; sp < NS; ++sp)
+            sum += *reinterpret_cast<const floatx4*>(P1 + (p1_rows_before(sp) + i) * ldp1 + c);
         const int nch = (min(n, kSymStrip * (si + 1)) + kSymChunk - 1) / kSymChunk;
-        const int64_t qstride = (int64_t)NS * kSymStrip * k;
-        sum += ordered_strided_sum(
-            P2 + ((int64_t)si * kSymStrip + (i - si * kSymStrip)) * k + c, nch, qstride);
-        P[(int64_t)i * ldP + c] = sum;
-        if (Hdot) acc += (double)Hdot[(int64_t)i * k + c] * (double)sum;
+        const int64_t qstride = (int64_t)NS * kSymStrip * ldp1;
+        const float* p2 = P2 + ((int64_t)si * kSymStrip + (i - si * kSymStrip)) * ldp1 + c;
+        for (int q = 0; q < nch; ++q) sum += *reinterpret_cast<const floatx4*>(p2 + q * qstride);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            if (c + j < k) {
+                P[(int64_t)i * ldP + c + j] = sum[j];
+                if (Hdot) acc += (double)Hdot[(int64_t)i * k + c + j] * (double)sum[j];
+            }
+        }
     }
     if (tr_part) {
         const double t = block_sum256(acc, redd);
@@ -406,7 +417,7 @@ SymPlan sym_plan(int n, int k) {
     p.ns = (n + kSymStrip - 1) / kSymStrip;
     p.nq = (n + kSymChunk - 1) / kSymChunk;
     p.p1_floats = (size_t)(p1_rows_before(p.ns - 1) + n) * p1_ld(k) + kSymSinkFloats;
-    p.p2_floats = (size_t)p.nq * p.ns * kSymStrip * k;
+    p.p2_floats = (size_t)p.nq * p.ns * kSymStrip * p1_ld(k);
     p.nkb_col = (n + 31) / 32;
     p.nkb_row = 2 * ((n + 63) / 64);
     p.packed_col_bytes = (size_t)p.nkb_col * p.nt * 3 * 64 * 16;
