@@ -18,7 +18,9 @@
  *     H, G, P are n x k with leading dimension k (dense).
  *   - The caller owns every buffer. The library allocates no device memory
  *     and frees nothing: scratch space is the caller's workspace `ws` of at
- *     least symnmf_workspace_bytes(...) bytes, 256-byte aligned.
+ *     least symnmf_workspace_bytes(...) bytes, 256-byte aligned. (The one
+ *     exception is symnmf_sh_noalloc's static 64 MiB device scratch, which
+ *     comes with the library's code object on each device it runs on.)
  *   - All device work is enqueued on `hip_stream` (a hipStream_t; NULL is the
  *     null stream). Calls that fill _host outputs synchronise that stream
  *     before they return; symnmf_labels is asynchronous.
