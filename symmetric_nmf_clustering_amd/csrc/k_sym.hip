@@ -14,25 +14,29 @@
 //
 // Both sides run on the bf16 matrix cores with exactly split fp32 operands
 // (bf16split.h). A wave owns 64 columns c0..c0+63 and reads a 32-row panel of
-// them as 8 float4 loads: load m gives lane l = 16g + c (g = l / 16) the four
-// columns c0 + 4c + q (q = 0..3) of row 4m + g, so each load instruction reads
-// 256 contiguous bytes of 4 rows (the pattern that streams fastest).
-//  * Column side: for fixed q the panel is a matrix-core B operand as loaded:
-//    column c0 + 4c + q along the lanes, the 32 rows within them (row 4e + g
-//    is element e of lane group g). A = H^T of the panel's rows in that K map
-//    (packed once, "column map"); the result lands as Z[column][factor].
-//  * Row side: the matrix core contracts over the index held within a lane,
-//    which here has to be the column. Multiplying each bf16 part (taken as an
-//    A operand) by a 0/1 selector on the matrix core returns it with the row
-//    along the lanes and 16 consecutive columns within each lane group, exactly
-//    (one nonzero term per output). The 64 columns then form two K blocks,
-//    columns c0 + 16g + 8h + e for half h; H's rows are packed in that map
-//    ("row map"), once per pass.
-//
-// The row-side products run as D^T = H^T (factor x column) times the parts
-// (column x row), so a lane ends with four consecutive factors of one row: the
-// per-panel sum over the eight waves is then one float2 per thread and one
-// store per thread (see reduce_rows).
+// them as 8 float4 buffer loads: load m gives lane l = 16g + c (g = l / 16)
+// the four columns c0 + 4c + q (q = 0..3) of row 4m + g, so each load
+// instruction reads 256 contiguous bytes of 4 rows. The panel's base is a
+// scalar and the lane offsets are fixed; rows past n read as zero (the buffer
+// ends at S's last row).
+//  * Column side: for fixed q the panel's parts are matrix-core B operands as
+//    loaded: column c0 + 4c + q along the lanes, the 32 rows within them (row
+//    4e + g is element e of lane group g). A = H^T of the panel's rows in that
+//    K order ("column map", packed once per pass); the result lands as
+//    Z[factor][column].
+//  * Row side: the contraction runs over the columns, which the loaded layout
+//    holds across lanes. Each wave writes the parts of one 16-row half of the
+//    panel to its own LDS area (eight bytes per lane, part and column: four
+//    rows of one column) and reads them back with the 16-bit transposed LDS
+//    read, which hands every lane eight consecutive columns of one row: the B
+//    operand of D^T = H^T (factor x column) times the part (column x row), with
+//    H's rows packed in column order ("row map"). A lane of the result holds
+//    four consecutive factors of one row, so the per-panel sum over the eight
+//    waves is one float2 per thread and one store per thread (reduce_rows).
+//  * A factor tile that holds at most 8 factors (the last one when k % 16 is
+//    1..8) carries two parts of H per operand, rows 8..15 of the tile holding
+//    the same factors as rows 0..7 (tile_mma): four matrix-core steps per K
+//    block instead of six. The two halves of the result are added at the end.
 //
 // Work: strips of 512 columns (8 waves), each walked down in chunks of 4096
 // rows. Workgroup (strip s, chunk qc) covers rows [4096 qc, min(4096 (qc+1),
@@ -55,6 +59,8 @@ namespace symnmf {
 namespace {
 
 constexpr int kSymWaves = kSymStrip / 64;  // waves per workgroup, 64 columns each
+// per wave: the three bf16 parts of one 16-row half of a panel (part_slot)
+constexpr int kSymPartBytes = 3 * 256 * 8;
 
 // rows of P1 held by the strips before strip s (each 512 (s' + 1) rows)
 __host__ __device__ inline int64_t p1_rows_before(int s) {
@@ -65,21 +71,67 @@ __host__ __device__ inline int p1_ld(int k) { return (k + 3) / 4 * 4; }
 // floats of the store sink after P1 (one float2 per thread of a workgroup)
 constexpr int kSymSinkFloats = 2 * 64 * kSymWaves;
 
-// (a, b) -> the bf16 pair of two fp32 values that are bf16-exact (their high
-// halves; a in the low half, as the matrix core reads a pair)
-__device__ __forceinline__ uint32_t pack_hi(float a, float b) {
-    return __builtin_amdgcn_perm(__builtin_bit_cast(uint32_t, b), __builtin_bit_cast(uint32_t, a),
-                                 0x07060302u);
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+// orders a wave's LDS accesses across lanes: what lanes wrote before it is
+// seen by the reads of other lanes after it
+__device__ __forceinline__ void wave_lds_sync() {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
-// H (n x k, ld k) -> B/A operands of every 32-row K block kb, 16-column tile t
-// and part p at out[((kb * NT + t) * 3 + p) * 64 + l], lane l = 16g + c holding
-// H[row(kb, g, e)][16t + c], e = 0..7, split exactly into three bf16 parts:
-//   column map: row = 32 kb + 4e + g
-//   row map:    row = 64 (kb / 2) + 16g + 8 (kb % 2) + e
-// Rows >= n and columns >= k are zero.
+// The 8-byte slot (of a part's 256) that holds quad b (rows 4e + b, e = 0..3,
+// of a 16-row half) of local column j. The low four bits are swizzled so that
+// the 16 lanes of a write (columns 4l + q of one quad) and the 16 lanes of a
+// transposed read (four columns of four quads) each touch 16 different 8-byte
+// bank groups.
+__device__ __forceinline__ int part_slot(int b, int j) {
+    return 64 * b + 16 * (j & 3) + (((j >> 2) ^ (4 * (j & 3) + b)) & 15);
+}
+
+// 16-bit transposed LDS read (gfx950): within each 16-lane group, lane 4a + b
+// reads four 16-bit values at its address, and lane 4b + e receives value e
+// of lane 4a + b as its element a (a, b, e = 0..3).
+__device__ __forceinline__ u32x2 lds_read_tr16(char* p) {
+    typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
+    const bf16x4 r = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
+        (lds_bf16x4*)((__attribute__((address_space(3))) char*)p));
+    return __builtin_bit_cast(u32x2, r);
+}
+
+// acc += A B over one 32-deep K block of one factor tile, A given by three
+// operands of H (sym_pack_kernel) and B by the three parts of S, smallest
+// terms first. A full tile takes the six terms of mfma_split6. A half tile
+// holds its (at most 8) factors in rows 0..7 of A and of the result; operand
+// 0 carries part 1 of H there and part 2 in rows 8..15, operand 1 part 3 and
+// operand 2 part 1 (rows 8..15 zero). The four products give the same six
+// terms: rows 0..7 get H1 S1, H3 S1, H1 S2, H1 S3, rows 8..15 get H2 S1, H2 S2.
+__device__ __forceinline__ floatx4 tile_mma(bool half, const u32x4 (&A)[3], const u32x4& b1,
+                                            const u32x4& b2, const u32x4& b3, floatx4 acc) {
+    if (half) {
+        acc = mfma_bf16(A[1], b1, acc);
+        acc = mfma_bf16(A[2], b3, acc);
+        acc = mfma_bf16(A[0], b2, acc);
+        acc = mfma_bf16(A[0], b1, acc);
+        return acc;
+    } else {
+        return mfma_split6(A[0], A[1], A[2], b1, b2, b3, acc);
+    }
+}
+
+// H (n x k, ld k) -> the A operands of every 32-row K block kb, tile t and
+// operand o at out[((kb * NT + t) * 3 + o) * 64 + l]: lane l = 16g + c holds
+// rows row(kb, g, e), e = 0..7, of factor slot c:
+//   column map: row = 32 kb + 4 e + g   (the K order of a loaded panel's rows)
+//   row map:    row = 32 kb + 8 g + e   (columns in order)
+// A full tile's operand o is part o + 1 (bf16split.h) of factor 16 t + c. A
+// half tile (the last one, when half) holds factor 16 t + (c & 7): operand 0
+// part 1 for c < 8 and part 2 for c >= 8, operands 1 and 2 parts 3 and 1 for
+// c < 8 and zero for c >= 8 (tile_mma). Rows >= n and factors >= k are zero.
 __global__ __launch_bounds__(256) void sym_pack_kernel(const float* __restrict__ H, int n, int k,
-                                                       int NT, int nkb, int rowmap,
+                                                       int NT, int half, int nkb, int rowmap,
                                                        u32x4* __restrict__ out,
                                                        const int* __restrict__ done) {
     if (done && *done) return;
@@ -90,22 +142,33 @@ __global__ __launch_bounds__(256) void sym_pack_kernel(const float* __restrict__
     const int tile = (int)(kt % NT);
     const int kb = (int)(kt / NT);
     const int g = lane >> 4;
-    const int c = 16 * tile + (lane & 15);
+    const int c = lane & 15;
+    const bool ht = half && tile == NT - 1;
+    const int f = 16 * tile + (ht ? (c & 7) : c);
     float v[8];
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
-        const int row = rowmap ? 64 * (kb >> 1) + 16 * g + 8 * (kb & 1) + e : 32 * kb + 4 * e + g;
-        v[e] = (row < n && c < k) ? H[(int64_t)row * k + c] : 0.f;
+        const int row = rowmap ? 32 * kb + 8 * g + e : 32 * kb + 4 * e + g;
+        v[e] = (row < n && f < k) ? H[(int64_t)row * k + f] : 0.f;
     }
     u32x4 x1, x2, x3;
     split3_8(v, x1, x2, x3);
+    if (ht) {
+        const u32x4 z = {0u, 0u, 0u, 0u};
+        const u32x4 o0 = c < 8 ? x1 : x2;
+        const u32x4 o1 = c < 8 ? x3 : z;
+        const u32x4 o2 = c < 8 ? x1 : z;
+        x1 = o0;
+        x2 = o1;
+        x3 = o2;
+    }
     u32x4* dst = out + kt * 3 * 64 + lane;
     dst[0] = x1;
     dst[64] = x2;
     dst[128] = x3;
 }
 
-template <int NT>
+template <int NT, bool HALF>
 __global__ __launch_bounds__(64 * kSymWaves) void sym_kernel(
     const float* __restrict__ S, int64_t lds, const u32x4* __restrict__ HsR,
     const u32x4* __restrict__ HsC, int n, int k, float* __restrict__ P1, float* __restrict__ P2,
@@ -117,6 +180,7 @@ __global__ __launch_bounds__(64 * kSymWaves) void sym_kernel(
     constexpr int HPER = (HB + NTH - 1) / NTH;
     __shared__ u32x4 hbuf[2][HB];
     __shared__ floatx4 red[2][WAVES][2][NT][64];
+    __shared__ __attribute__((aligned(16))) char parts[WAVES][kSymPartBytes];
 
     const int s = blockIdx.x;
     const int qc = blockIdx.y;
@@ -138,7 +202,7 @@ __global__ __launch_bounds__(64 * kSymWaves) void sym_kernel(
     const int b0 = c0 >> 5;                    // its first 32-column block
     const bool active = c0 < n;
 
-    // row side B operands (row map) of the wave's two K blocks, for the chunk
+    // row side A operands (row map) of the wave's two K blocks, for the chunk
     u32x4 hj[2][NT][3];
     {
         const int G = min(c0 >> 6, ngr - 1);
@@ -150,32 +214,24 @@ __global__ __launch_bounds__(64 * kSymWaves) void sym_kernel(
                 for (int p = 0; p < 3; ++p)
                     hj[h][t][p] = HsR[(((2 * G + h) * NT + t) * 3 + p) * 64 + lane];
     }
-    // sel[rho]: picks row 16 rho + lr of a panel in the column map (row 4e + g
-    // is element e of lane group g): bf16 1.0 at element 4 rho + lr / 4 of lane
-    // group lr % 4, zero elsewhere
-    u32x4 sel[2];
-#pragma unroll
-    for (int rho = 0; rho < 2; ++rho)
-#pragma unroll
-        for (int w2 = 0; w2 < 4; ++w2) {
-            const int e = 4 * rho + (lr >> 2);
-            const bool hit = g == (lr & 3) && (e >> 1) == w2;
-            sel[rho][w2] = hit ? (e & 1 ? 0x3F800000u : 0x00003F80u) : 0u;
-        }
     // a float4 that would start at column >= n (ragged edge, or a wave past n)
-    // reads the row's first 16 bytes instead, so no load sits in a branch; the
-    // values at columns >= n are zeroed before use. A float4 starting below n
-    // lies inside the row (lds is a multiple of 4).
+    // reads the row's first 16 bytes instead; the values at columns >= n are
+    // zeroed before use. A float4 starting below n lies inside the row (lds is
+    // a multiple of 4).
     const int col = c0 + 4 * lr;
     const int coff = col < n ? col : 0;
+    const int voff = (g * (int)lds + coff) * 4;  // bytes; 32 rows of S stay below 2^31
 
     typedef floatx4 Panel[8];
     auto load = [&](int a, Panel& v) {
+        const int64_t row0 = 32 * (int64_t)a;
+        const int64_t rest = ((int64_t)n - row0) * lds * 4;  // bytes from the panel to S's end
+        const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+            (void*)(S + row0 * lds), (short)0, (int)min(rest, (int64_t)0x7fffffff), 0x00020000);
 #pragma unroll
-        for (int m = 0; m < 8; ++m) {
-            const float* rp = S + (int64_t)min(32 * a + 4 * m + g, n - 1) * lds + coff;
-            v[m] = __builtin_nontemporal_load(reinterpret_cast<const floatx4*>(rp));
-        }
+        for (int m = 0; m < 8; ++m)
+            v[m] = __builtin_bit_cast(
+                floatx4, __builtin_amdgcn_raw_buffer_load_b128(rs, voff + m * 16 * (int)lds, 0, 2));
     };
     u32x4 hst[HPER];
     auto load_h = [&](int a) {
@@ -197,6 +253,21 @@ __global__ __launch_bounds__(64 * kSymWaves) void sym_kernel(
 #pragma unroll
         for (int t = 0; t < NT; ++t) acc2[q][t] = floatx4{0.f, 0.f, 0.f, 0.f};
     const int64_t p1base = p1_rows_before(s);
+
+    // the wave's parts area: lane (lr, g) writes quad g of columns 4 lr + q;
+    // lane 4a + b of group g reads quad b of columns 32 h + 8 g + 4 r + a
+    char* const area = parts[wave];
+    const int la = lr >> 2, lb = lr & 3;
+    // a half tile's rows 8..15 (lanes 32..63) added to its rows 0..7 (lanes
+    // 0..31) through the wave's area (free between panels); lanes 32..63 of
+    // the result are not used
+    auto fold_half = [&](floatx4 (&x)[4], int cnt) {
+        floatx4* const st = reinterpret_cast<floatx4*>(area);
+        for (int j = 0; j < cnt; ++j) st[64 * j + lane] = x[j];
+        wave_lds_sync();
+        for (int j = 0; j < cnt; ++j) x[j] += st[64 * j + (lane ^ 32)];
+        wave_lds_sync();
+    };
 
     auto compute = [&](int a, Panel& v) {
         const int hb = a & 1;
@@ -229,7 +300,11 @@ __global__ __launch_bounds__(64 * kSymWaves) void sym_kernel(
             }
             if (a <= b0) {
                 const bool ck = a < b0 + (lr >> 3);  // the diagonal block is row side only
-                const u32x4* hl = &hbuf[hb][lane];
+                u32x4 hc[NT][3];
+#pragma unroll
+                for (int t = 0; t < NT; ++t)
+#pragma unroll
+                    for (int o = 0; o < 3; ++o) hc[t][o] = hbuf[hb][(3 * t + o) * 64 + lane];
 #pragma unroll
                 for (int q = 0; q < 4; ++q) {
                     u32x4 z1 = y[q][0], z2 = y[q][1], z3 = y[q][2];
@@ -240,48 +315,46 @@ __global__ __launch_bounds__(64 * kSymWaves) void sym_kernel(
                     }
 #pragma unroll
                     for (int t = 0; t < NT; ++t)
-                        acc2[q][t] = mfma_split6(hl[(3 * t) * 64], hl[(3 * t + 1) * 64],
-                                                 hl[(3 * t + 2) * 64], z1, z2, z3, acc2[q][t]);
+                        acc2[q][t] = tile_mma(HALF && t == NT - 1, hc[t], z1, z2, z3, acc2[q][t]);
                 }
             }
-            // row side, one part at a time (smallest first): the part with the
-            // row along the lanes, then its terms of the six-term product
+            // row side, one 16-row half at a time: element pair 2 rho, 2 rho + 1
+            // of y[q][p] is quad g (rows 4e + g, e = 0..3) of that half
 #pragma unroll
-            for (int p = 2; p >= 0; --p) {
+            for (int rho = 0; rho < 2; ++rho) {
 #pragma unroll
-                for (int rho = 0; rho < 2; ++rho) {
-                    floatx4 d[4];
+                for (int q = 0; q < 4; ++q)
 #pragma unroll
-                    for (int q = 0; q < 4; ++q)
-                        d[q] = mfma_bf16(y[q][p], sel[rho], floatx4{0.f, 0.f, 0.f, 0.f});
-                    // lane (lr, g') now holds part p of row 32a + 16 rho + lr,
-                    // columns c0 + 16 g' + 4 r + q in d[q][r]; K block h takes
-                    // columns c0 + 16 g' + 8 h + e, e = 4 (r - 2h) + q
+                    for (int p = 0; p < 3; ++p)
+                        *reinterpret_cast<u32x2*>(area + p * 2048 + 8 * part_slot(g, 4 * lr + q)) =
+                            u32x2{y[q][p][2 * rho], y[q][p][2 * rho + 1]};
+                wave_lds_sync();
 #pragma unroll
-                    for (int h = 0; h < 2; ++h) {
-                        const u32x4 ap = {pack_hi(d[0][2 * h], d[1][2 * h]),
-                                          pack_hi(d[2][2 * h], d[3][2 * h]),
-                                          pack_hi(d[0][2 * h + 1], d[1][2 * h + 1]),
-                                          pack_hi(d[2][2 * h + 1], d[3][2 * h + 1])};
+                for (int h = 0; h < 2; ++h) {
+                    // B operand of part p: lane (N, g) holds columns 32 h + 8 g .. + 7
+                    // of row 16 rho + 4 (N & 3) + (N >> 2)
+                    u32x4 bp[3];
 #pragma unroll
-                        for (int t = 0; t < NT; ++t) {
-                            // the terms a_p b_r with p + r <= 4 (parts numbered 1..3)
-                            // as D^T: hj (H^T, factor x column) is the A
-                            // operand and the part (column x row) the B one
-                            if (p == 2) {
-                                acc1[rho][t] = mfma_bf16(hj[h][t][0], ap, acc1[rho][t]);
-                            } else if (p == 1) {
-                                acc1[rho][t] = mfma_bf16(hj[h][t][1], ap, acc1[rho][t]);
-                                acc1[rho][t] = mfma_bf16(hj[h][t][0], ap, acc1[rho][t]);
-                            } else {
-                                acc1[rho][t] = mfma_bf16(hj[h][t][2], ap, acc1[rho][t]);
-                                acc1[rho][t] = mfma_bf16(hj[h][t][1], ap, acc1[rho][t]);
-                                acc1[rho][t] = mfma_bf16(hj[h][t][0], ap, acc1[rho][t]);
-                            }
-                        }
+                    for (int p = 0; p < 3; ++p) {
+                        const u32x2 lo =
+                            lds_read_tr16(area + p * 2048 + 8 * part_slot(lb, 32 * h + 8 * g + la));
+                        const u32x2 hi = lds_read_tr16(
+                            area + p * 2048 + 8 * part_slot(lb, 32 * h + 8 * g + 4 + la));
+                        bp[p] = u32x4{lo[0], lo[1], hi[0], hi[1]};
                     }
+#pragma unroll
+                    for (int t = 0; t < NT; ++t)
+                        acc1[rho][t] =
+                            tile_mma(HALF && t == NT - 1, hj[h][t], bp[0], bp[1], bp[2], acc1[rho][t]);
                 }
+                wave_lds_sync();  // the next writes to the area come after these reads
             }
+        }
+        if constexpr (HALF) {
+            floatx4 hx[4] = {acc1[0][NT - 1], acc1[1][NT - 1]};
+            fold_half(hx, 2);
+            acc1[0][NT - 1] = hx[0];
+            acc1[1][NT - 1] = hx[1];
         }
 #pragma unroll
         for (int rho = 0; rho < 2; ++rho)
@@ -290,14 +363,14 @@ __global__ __launch_bounds__(64 * kSymWaves) void sym_kernel(
     };
 
     // The waves' row-side sums of panel a, in wave order, to P1. Lane
-    // (lr, g') of acc1[rho][t] holds factors 16 t + 4 g' .. +3 of row
-    // 32 a + 16 rho + lr, so thread h sums one float2 (half h & 1 of the
-    // float4 at h >> 1 of each wave's block) over the eight waves and stores
-    // it. Every thread stores exactly once (a thread without an output, or
-    // an output past n or past k, writes the sink): with no branch around
-    // the store, the compiler counts it exactly and never waits for it when
-    // it waits for the next panel's loads (a store in a branch made every
-    // panel wait for the previous panel's stores to complete).
+    // (N, g') of acc1[rho][t] holds factors 16 t + 4 g' .. +3 of row
+    // 32 a + 16 rho + 4 (N & 3) + (N >> 2), so thread h sums one float2 (half
+    // h & 1 of the float4 at h >> 1 of each wave's block) over the eight
+    // waves and stores it. Every thread stores exactly once (a thread without
+    // an output, or an output past n or past k, writes the sink): with no
+    // branch around the store, the compiler counts it exactly and never waits
+    // for it when it waits for the next panel's loads (a store in a branch
+    // made every panel wait for the previous panel's stores to complete).
     const int ldp1 = p1_ld(k);
     float* __restrict__ sink = P1 + (p1_rows_before(NS - 1) + n) * (int64_t)ldp1 + 2 * tid;
     auto reduce_rows = [&](int a) {
@@ -311,7 +384,8 @@ __global__ __launch_bounds__(64 * kSymWaves) void sym_kernel(
         const int o = h >> 1;
         const int ln = o & 63, t = (o >> 6) % NT, rho = o / (64 * NT);
         const int fq = 16 * t + 4 * (ln >> 4) + 2 * (h & 1);
-        const int i = 32 * a + 16 * rho + (ln & 15);
+        const int N = ln & 15;
+        const int i = 32 * a + 16 * rho + 4 * (N & 3) + (N >> 2);
         const bool ok = tid < HALVES && fq < k && i < n;
         float* dstp = ok ? P1 + (p1base + i) * ldp1 + fq : sink;
         *reinterpret_cast<f32x2*>(dstp) = sum;
@@ -343,8 +417,14 @@ __global__ __launch_bounds__(64 * kSymWaves) void sym_kernel(
     }
 
     // column side of the chunk: lane (lr, g') holds column c0 + 4 lr + q,
-    // factor columns 16t + 4g' + r
+    // factors 16t + 4g' + r (a half tile's rows 8..15 folded into 0..7 first)
     // (rows of p1_ld(k) floats: one float4 of four factors per store)
+    if constexpr (HALF) {
+        floatx4 hx[4] = {acc2[0][NT - 1], acc2[1][NT - 1], acc2[2][NT - 1], acc2[3][NT - 1]};
+        fold_half(hx, 4);
+#pragma unroll
+        for (int q = 0; q < 4; ++q) acc2[q][NT - 1] = hx[q];
+    }
     float* __restrict__ dst = P2 + ((int64_t)qc * NS + s) * kSymStrip * ldp1;
 #pragma unroll
     for (int q = 0; q < 4; ++q)
@@ -422,6 +502,7 @@ SymPlan sym_plan(int n, int k) {
     p.nkb_row = 2 * ((n + 63) / 64);
     p.packed_col_bytes = (size_t)p.nkb_col * p.nt * 3 * 64 * 16;
     p.packed_row_bytes = (size_t)p.nkb_row * p.nt * 3 * 64 * 16;
+    p.half = k % 16 != 0 && k % 16 <= 8;
     return p;
 }
 
@@ -431,7 +512,7 @@ hipError_t launch_sym_pack(const float* H, int n, int k, const SymPlan& p, void*
         const int nkb = rowmap ? p.nkb_row : p.nkb_col;
         const int64_t threads = (int64_t)nkb * p.nt * 64;
         hipLaunchKernelGGL(sym_pack_kernel, dim3((unsigned)((threads + 255) / 256)), dim3(256), 0,
-                           st, H, n, k, p.nt, nkb, rowmap,
+                           st, H, n, k, p.nt, (int)p.half, nkb, rowmap,
                            static_cast<u32x4*>(rowmap ? HsR : HsC), done);
         const hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
@@ -446,15 +527,15 @@ hipError_t launch_sym(const float* S, int64_t lds, const void* HsR, const void* 
     const u32x4* hc = static_cast<const u32x4*>(HsC);
     const dim3 grid((unsigned)p.ns, (unsigned)p.nq);
     const dim3 block(64 * kSymWaves);
-    switch (p.nt) {
-        case 1:
-            hipLaunchKernelGGL((sym_kernel<1>), grid, block, 0, st, S, lds, hr, hc, n, k, P1, P2, done);
-            break;
-        case 2:
-            hipLaunchKernelGGL((sym_kernel<2>), grid, block, 0, st, S, lds, hr, hc, n, k, P1, P2, done);
-            break;
-        default: return hipErrorInvalidValue;
-    }
+#define SYMNMF_SYM_LAUNCH(NT_, HALF_)                                                         \
+    hipLaunchKernelGGL((sym_kernel<NT_, HALF_>), grid, block, 0, st, S, lds, hr, hc, n, k, P1, P2, \
+                       done)
+    if (p.nt == 1 && !p.half) SYMNMF_SYM_LAUNCH(1, false);
+    else if (p.nt == 1) SYMNMF_SYM_LAUNCH(1, true);
+    else if (p.nt == 2 && !p.half) SYMNMF_SYM_LAUNCH(2, false);
+    else if (p.nt == 2) SYMNMF_SYM_LAUNCH(2, true);
+    else return hipErrorInvalidValue;
+#undef SYMNMF_SYM_LAUNCH
     return hipGetLastError();
 }
 

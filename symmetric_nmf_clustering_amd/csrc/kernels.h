@@ -102,6 +102,7 @@ struct SymPlan {
     int nkb_col, nkb_row;     // K blocks of the two packings of H
     size_t packed_col_bytes;  // sizes of the two packings
     size_t packed_row_bytes;
+    bool half;                // the last tile holds at most 8 factors (two parts per operand)
 };
 SymPlan sym_plan(int n, int k);
 // `done` (nullable, device): a set flag skips the launch's work (a fit that

@@ -36,7 +36,7 @@ COPY_REPS = 3
 # the full S.H pass: contiguous row splits (row mode 0)
 FULL_PASS = re.compile(r"sh_panel_kernel<(\d+), (\d+), (\d+), (true|false), 0>")
 # the upper-triangle pass
-SYM_PASS = re.compile(r"sym_kernel<(\d+)>")
+SYM_PASS = re.compile(r"sym_kernel<(\d+), (true|false)>")
 KERNELS = {
     # op: (dispatch name pattern, source file, algorithmic bytes per launch)
     "sh": (FULL_PASS, "k_sh.hip", lambda n, k: 4.0 * n * n + 8.0 * n * k),

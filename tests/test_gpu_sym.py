@@ -14,7 +14,7 @@ pytestmark = pytest.mark.gpu
 # Bound on |P - S H| relative to sum_j |S_ij H_jc| (the size of the terms):
 # a dropped split term (x1 y2 is 2^-8 of x y), a block counted twice or
 # missed, or a transposed block read as itself shows as 1e-3 or more. The
-# bound allows fp32 accumulation: a column-side accumulator takes 6 matrix-core
+# bound allows fp32 accumulation: a column-side accumulator takes 4 or 6 matrix-core
 # steps per 32-row panel over up to 128 panels of a chunk, then the strip and
 # chunk partials are added in the fold.
 REL = 2e-5
