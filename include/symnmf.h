@@ -179,7 +179,8 @@ size_t symnmf_workspace_bytes(int op, int64_t n, int32_t k_or_p, int64_t T,
  * window X (T x n, fp32, ldx) on the device.
  *   kind = SYMNMF_ABSCORR (P1 introduction: absolute Pearson correlation):
  *     z_ti = (x_ti - mu_i)/||x_.i - mu_i||_2 (moments in fp64), S = |Z^T Z|,
- *     a fp32 MFMA contraction over the T days; the diagonal is kept.
+ *     a contraction over the T days on the bf16 matrix cores with exactly
+ *     split fp32 operands (fp32 products, fp32 sums); the diagonal is kept.
  *     tail_frac is ignored.
  *   kind = SYMNMF_TPDM (P1 introduction; P3): losses -X, per-column ordinal
  *     ranks R (ties to the earlier day), F = R/(T+1), Frechet alpha = 2 margins
@@ -187,7 +188,7 @@ size_t symnmf_workspace_bytes(int op, int64_t n, int32_t k_or_p, int64_t T,
  *     m = ceil(tail_frac T - 1e-4) largest-radius days (ties to the earlier day;
  *     the 1e-4 slack keeps a float tail_frac whose product with T is an
  *     integer up to rounding at that integer),
- *     theta_t = x_t./r_t, S = (1/m) Theta^T Theta (MFMA, K = m).
+ *     theta_t = x_t./r_t, S = (1/m) Theta^T Theta (fp32 MFMA, K = m).
  * S is computed on upper-triangle tiles and mirrored, so it is bitwise
  * symmetric. Every element of S (columns < n of rows < n) is written.
  * S_fro2_host (nullable) receives ||S||_F^2 (fp64).

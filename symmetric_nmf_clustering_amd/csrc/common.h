@@ -17,6 +17,15 @@ __device__ __forceinline__ floatx4 mfma16x16x4(float a, float b, floatx4 c) {
     return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
 }
 
+// Orders a wave's LDS accesses across its lanes: what lanes wrote before it is
+// seen by the reads of other lanes after it (the wave's LDS operations run in
+// order; this keeps the compiler from moving them across).
+__device__ __forceinline__ void wave_lds_sync() {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
 // SplitMix64 (Steele, Lea and Flood, OOPSLA 2014): output c+1 of the
 // sequence whose state starts at `key`.
 __host__ __device__ __forceinline__ uint64_t splitmix64(uint64_t key, uint64_t c) {

@@ -6,6 +6,7 @@
 // tile and mirrored so that S is bitwise symmetric.
 #include <math.h>
 
+#include "bf16split.h"
 #include "common.h"
 #include "kernels.h"
 
@@ -225,7 +226,7 @@ hipError_t launch_tpdm_theta(const int* R, int T, int n, const int* sel, const d
 
 // ---- MFMA Gram with mirrored upper-triangle tiles -------------------------------
 // Workgroup tile 128 x 128 of S (waves 2 x 2, 64 x 64 each), tiles (I, J) with
-// I <= J only. Per 4-day step a lane loads one float4 of the A panel
+// I <= J only. In the fp32 path, per 4-day step a lane loads one float4 of the A panel
 // (day t0 + lane/16, columns i0 + 4 (lane%16) .. +3) and one of the B panel;
 // element qa of the A float4 and qb of the B float4 feed MFMA tile (qa, qb),
 // which owns S[i0 + 4 m + qa][j0 + 4 n + qb]. The result element r of tile
@@ -247,6 +248,15 @@ __device__ __forceinline__ void decode_upper(int64_t b, int& I, int& J) {
     I = (int)(b - j * (j + 1) / 2);
 }
 
+// SPLIT: 32-day steps on the bf16 matrix cores with exactly split operands
+// (bf16split.h; Kp % 32 == 0). Lane l = 16g + c loads, per step, the float4s
+// of days 32 ks + 4 m + g (m = 0..7) at columns i0 + 4c .. +3 (A) and
+// j0 + 4c .. +3 (B): element m of column 4c + q is element m of lane group g
+// of a 16x16x32 operand, the same K order on both sides, so A's column q and
+// B's column q' feed tile (q, q') with its result in the same lanes as the
+// fp32 path's. Six products per operand pair (fp32-exact), against 32 fp32
+// 16x16x4 steps per 32 days in the fp32 path.
+template <bool SPLIT>
 __global__ __launch_bounds__(256) void gram_build_kernel(const float* __restrict__ Z, int Kp,
                                                          int64_t ldz, int n, float scale,
                                                          int absval, float* __restrict__ S,
@@ -257,6 +267,7 @@ __global__ __launch_bounds__(256) void gram_build_kernel(const float* __restrict
     // each XCD a contiguous run of tiles (they share Z panels through its L2).
     const int64_t b = (int64_t)(blockIdx.x % 8) * chunk + blockIdx.x / 8;
     __shared__ double red[4];
+    __shared__ floatx4 mir[4][64 * 16];  // per wave: a 64 x 64 tile of S^T (16 KiB)
     if (b >= ntiles) return;
     int I, J;
     decode_upper(b, I, J);
@@ -278,18 +289,56 @@ __global__ __launch_bounds__(256) void gram_build_kernel(const float* __restrict
         for (int a = 0; a < 4; ++a)
 #pragma unroll
             for (int c = 0; c < 4; ++c) acc[a][c] = floatx4{0.f, 0.f, 0.f, 0.f};
-        const float* Ap = Z + i0 + 4 * cl;
-        const float* Bp = Z + j0 + 4 * cl;
-        for (int t0 = 0; t0 < Kp; t0 += 4) {
-            const int64_t off = (int64_t)(t0 + r) * ldz;
-            const float4 av = *reinterpret_cast<const float4*>(Ap + off);
-            const float4 bv = *reinterpret_cast<const float4*>(Bp + off);
-            const float a4[4] = {av.x, av.y, av.z, av.w};
-            const float b4[4] = {bv.x, bv.y, bv.z, bv.w};
+        if constexpr (SPLIT) {
+            const float* Ap = Z + (int64_t)r * ldz + i0 + 4 * cl;
+            const float* Bp = Z + (int64_t)r * ldz + j0 + 4 * cl;
+            floatx4 ra[8], rb[8];
+            auto load = [&](int ks) {
+                const int64_t off = (int64_t)32 * ks * ldz;
 #pragma unroll
-            for (int qa = 0; qa < 4; ++qa)
+                for (int m = 0; m < 8; ++m) {
+                    ra[m] = *reinterpret_cast<const floatx4*>(Ap + off + (int64_t)4 * m * ldz);
+                    rb[m] = *reinterpret_cast<const floatx4*>(Bp + off + (int64_t)4 * m * ldz);
+                }
+            };
+            const int nks = Kp / 32;
+            load(0);
+            for (int ks = 0; ks < nks; ++ks) {
+                u32x4 ya[4][3], yb[4][3];
 #pragma unroll
-                for (int qb = 0; qb < 4; ++qb) acc[qa][qb] = mfma16x16x4(a4[qa], b4[qb], acc[qa][qb]);
+                for (int q = 0; q < 4; ++q) {
+                    float ca[8], cb[8];
+#pragma unroll
+                    for (int m = 0; m < 8; ++m) {
+                        ca[m] = ra[m][q];
+                        cb[m] = rb[m][q];
+                    }
+                    split3_8(ca, ya[q][0], ya[q][1], ya[q][2]);
+                    split3_8(cb, yb[q][0], yb[q][1], yb[q][2]);
+                }
+                load(min(ks + 1, nks - 1));  // the next step's days, in flight during the products
+#pragma unroll
+                for (int qa = 0; qa < 4; ++qa)
+#pragma unroll
+                    for (int qb = 0; qb < 4; ++qb)
+                        acc[qa][qb] = mfma_split6(ya[qa][0], ya[qa][1], ya[qa][2], yb[qb][0],
+                                                  yb[qb][1], yb[qb][2], acc[qa][qb]);
+            }
+        } else {
+            const float* Ap = Z + i0 + 4 * cl;
+            const float* Bp = Z + j0 + 4 * cl;
+            for (int t0 = 0; t0 < Kp; t0 += 4) {
+                const int64_t off = (int64_t)(t0 + r) * ldz;
+                const float4 av = *reinterpret_cast<const float4*>(Ap + off);
+                const float4 bv = *reinterpret_cast<const float4*>(Bp + off);
+                const float a4[4] = {av.x, av.y, av.z, av.w};
+                const float b4[4] = {bv.x, bv.y, bv.z, bv.w};
+#pragma unroll
+                for (int qa = 0; qa < 4; ++qa)
+#pragma unroll
+                    for (int qb = 0; qb < 4; ++qb)
+                        acc[qa][qb] = mfma16x16x4(a4[qa], b4[qb], acc[qa][qb]);
+            }
         }
 #pragma unroll
         for (int qa = 0; qa < 4; ++qa)
@@ -325,25 +374,38 @@ __global__ __launch_bounds__(256) void gram_build_kernel(const float* __restrict
                         if (jj + 3 < n) fro += 2.0 * (double)v.w * v.w;
                     }
                 }
-            const int ii = i0 + 16 * r;
+            // the mirror S^T of the block, turned in the wave's LDS tile: lane
+            // (r, cl) puts the float4 of rows i0 + 16 r + 4 e .. +3 of column
+            // j0 + 4 cl + qb into tile row 4 cl + qb, 16-byte slot 4 r + e, and
+            // tile rows come back whole, so each store writes 256 contiguous
+            // bytes of four rows of S (written straight from the lanes, a
+            // store covered 64 bytes of each of 16 rows, which cost a third of
+            // the build). Slot s of tile row t sits at s ^ (t / 4): the 16
+            // lanes of a write and of a read each touch 16 bank groups.
+            floatx4* const tile = mir[wave];
 #pragma unroll
             for (int qb = 0; qb < 4; ++qb)
 #pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    const int j = j0 + 4 * cl + qb;
-                    const int ic = ii + 4 * e;
-                    const float4 v = {acc[0][qb][e], acc[1][qb][e], acc[2][qb][e], acc[3][qb][e]};
-                    if (j < n) {
-                        float* dst = S + (int64_t)j * lds + ic;
-                        if (ic + 4 <= n) {
-                            *reinterpret_cast<float4*>(dst) = v;
-                        } else {
-                            if (ic < n) dst[0] = v.x;
-                            if (ic + 1 < n) dst[1] = v.y;
-                            if (ic + 2 < n) dst[2] = v.z;
-                        }
+                for (int e = 0; e < 4; ++e)
+                    tile[(4 * cl + qb) * 16 + ((4 * r + e) ^ cl)] =
+                        floatx4{acc[0][qb][e], acc[1][qb][e], acc[2][qb][e], acc[3][qb][e]};
+            wave_lds_sync();
+            const int ic = i0 + 4 * cl;
+#pragma unroll
+            for (int t = 0; t < 16; ++t) {
+                const int j = j0 + 4 * t + r;
+                const floatx4 v = tile[(4 * t + r) * 16 + (cl ^ t)];
+                if (j < n) {
+                    float* dst = S + (int64_t)j * lds + ic;
+                    if (ic + 4 <= n) {
+                        *reinterpret_cast<floatx4*>(dst) = v;
+                    } else {
+                        if (ic < n) dst[0] = v[0];
+                        if (ic + 1 < n) dst[1] = v[1];
+                        if (ic + 2 < n) dst[2] = v[2];
                     }
                 }
+            }
         } else {
             // diagonal block: element (i, j) with i <= j is written at (i, j)
             // and, for i < j, mirrored to (j, i); i > j is left to its mirror
@@ -373,13 +435,18 @@ __global__ __launch_bounds__(256) void gram_build_kernel(const float* __restrict
 }
 
 hipError_t launch_gram_build(const float* Z, int Kp, int64_t ldz, int n, float scale, int absval,
-                             float* S, int64_t lds, double* part2, int64_t* ntiles_out,
-                             hipStream_t st) {
+                             bool split, float* S, int64_t lds, double* part2,
+                             int64_t* ntiles_out, hipStream_t st) {
+    if (Kp % (split ? 32 : 4)) return hipErrorInvalidValue;
     const int64_t ntiles = gram_build_tiles(n);
     const int64_t chunk = (ntiles + 7) / 8;
     if (ntiles_out) *ntiles_out = ntiles;
-    hipLaunchKernelGGL(gram_build_kernel, dim3((unsigned)(chunk * 8)), dim3(256), 0, st, Z, Kp,
-                       ldz, n, scale, absval, S, lds, ntiles, chunk, part2);
+    if (split)
+        hipLaunchKernelGGL(gram_build_kernel<true>, dim3((unsigned)(chunk * 8)), dim3(256), 0, st,
+                           Z, Kp, ldz, n, scale, absval, S, lds, ntiles, chunk, part2);
+    else
+        hipLaunchKernelGGL(gram_build_kernel<false>, dim3((unsigned)(chunk * 8)), dim3(256), 0, st,
+                           Z, Kp, ldz, n, scale, absval, S, lds, ntiles, chunk, part2);
     return hipGetLastError();
 }
 

@@ -74,14 +74,6 @@ constexpr int kSymSinkFloats = 2 * 64 * kSymWaves;
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
-// orders a wave's LDS accesses across lanes: what lanes wrote before it is
-// seen by the reads of other lanes after it
-__device__ __forceinline__ void wave_lds_sync() {
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-}
-
 // The 8-byte slot (of a part's 256) that holds quad b (rows 4e + b, e = 0..3,
 // of a 16-row half) of local column j. The low four bits are swizzled so that
 // the 16 lanes of a write (columns 4l + q of one quad) and the 16 lanes of a

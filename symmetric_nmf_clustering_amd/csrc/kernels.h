@@ -204,11 +204,13 @@ hipError_t launch_tpdm_select(const int* hist, int T, int m, double* radius, int
                               hipStream_t st);
 hipError_t launch_tpdm_theta(const int* R, int T, int n, const int* sel, const double* radius,
                              int m, int mp, float* Theta, int64_t ldz, hipStream_t st);
-// S = scale * (|A^T A| if absval else A^T A), A = Z (Kp x ldz, Kp % 4 == 0),
-// upper-triangle tiles mirrored; part2[tile] = partial ||S||^2 (fp64).
+// S = scale * (|A^T A| if absval else A^T A), A = Z (Kp x ldz), upper-triangle
+// tiles mirrored; part2[tile] = partial ||S||^2 (fp64). split: the bf16 matrix
+// cores with exactly split operands, Kp % 32 == 0; otherwise fp32 MFMA,
+// Kp % 4 == 0 (another Kp: hipErrorInvalidValue).
 hipError_t launch_gram_build(const float* Z, int Kp, int64_t ldz, int n, float scale, int absval,
-                             float* S, int64_t lds, double* part2, int64_t* ntiles_out,
-                             hipStream_t st);
+                             bool split, float* S, int64_t lds, double* part2,
+                             int64_t* ntiles_out, hipStream_t st);
 int64_t gram_build_tiles(int n);
 hipError_t launch_sum_doubles(const double* part, int64_t count, double* out, hipStream_t st);
 

@@ -512,7 +512,8 @@ size_t build_layout(void* ws, int kind, int64_t T, int64_t n, BuildLayout* L) {
     const int64_t ldz = round_up(n, kGramTile);
     BuildLayout l{};
     if (kind == SYMNMF_ABSCORR) {
-        l.Z = c.take<float>((size_t)round_up(T, 4) * ldz);
+        // days padded to whole 32-day steps of the split Gram pass
+        l.Z = c.take<float>((size_t)round_up(T, 32) * ldz);
     } else {
         // Theta needs m_p = round_up(ceil(tail_frac T), 4) <= round_up(T, 4) rows
         l.Z = c.take<float>((size_t)round_up(T, 4) * ldz);
@@ -738,8 +739,13 @@ int symnmf_build_S(int kind, const float* X, int64_t T, int64_t n, int64_t ldx, 
     int Kp = 0;
     float scale = 1.f;
     int absval = 1;
+    bool split = false;
     if (kind == SYMNMF_ABSCORR) {
-        Kp = (int)round_up(T, 4);
+        // the T-deep contraction runs on the bf16 matrix cores (exact split
+        // operands); the TPDM's few extreme days (m = ceil(tail_frac T)) stay
+        // on the fp32 path, where padding m to 32 days would cost more
+        Kp = (int)round_up(T, 32);
+        split = true;
         HIPCHK(launch_standardize(X, (int)T, (int)n, ldx, L.Z, Kp, ldz, L.flags, st));
     } else {
         // m = ceil(tail_frac T) extreme days
@@ -767,8 +773,8 @@ int symnmf_build_S(int kind, const float* X, int64_t T, int64_t n, int64_t ldx, 
     {
         // algorithmic traffic: S written once (4 n^2 bytes) plus the panels read
         ProfScope ps(SYMNMF_PROF_BUILD_GRAM, 4.0 * n * (double)n + 4.0 * Kp * (double)n, st);
-        HIPCHK(launch_gram_build(L.Z, Kp, ldz, (int)n, scale, absval, S, lds, L.part2, &ntiles,
-                                 st));
+        HIPCHK(launch_gram_build(L.Z, Kp, ldz, (int)n, scale, absval, split, S, lds, L.part2,
+                                 &ntiles, st));
     }
     if (S_fro2_host) {
         HIPCHK(launch_sum_doubles(L.part2, ntiles, L.fro, st));
