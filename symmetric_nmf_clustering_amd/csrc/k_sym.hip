@@ -431,42 +431,54 @@ __global__ __launch_bounds__(64 * kSymWaves) void sym_kernel(
 
 // P[i][c] (ld ldP) = sum over s >= i / 512 of P1[s][i][c], then over the chunks of
 // strip i / 512 of P2[qc][s(i)][i][c]; tr_part[b] = sum over the rows of block
-// b of <Hdot_i, P_i> (fp64), blocks of kUpdRows rows. A thread sums four
-// factors at once (float4 loads of the p1_ld(k)-float rows of P1 and P2), each
-// in the same order as a scalar sum would.
-__global__ __launch_bounds__(256) void sym_fold_kernel(const float* __restrict__ P1,
+// b of <Hdot_i, P_i> (fp64), blocks of kUpdRows rows. One thread per row and
+// four factors (blockDim = kUpdRows * p1_ld(k) / 4: float4 loads of the
+// p1_ld(k)-float rows of P1 and P2), each summed in the same order as a scalar
+// sum would. A row adds up to ns strip partials (rows near the top the most)
+// and up to n / 4096 chunk partials (rows near the bottom): kFoldInFlight and
+// 8 loads are issued before their additions, so neither sum waits for a
+// memory round trip per partial.
+constexpr int kFoldInFlight = 16;
+__global__ __launch_bounds__(512) void sym_fold_kernel(const float* __restrict__ P1,
                                                        const float* __restrict__ P2, int n, int k,
                                                        int NS, float* __restrict__ P, int ldP,
                                                        const float* __restrict__ Hdot,
                                                        double* __restrict__ tr_part,
                                                        const int* __restrict__ done) {
     if (done && *done) return;
-    __shared__ double redd[4];
+    __shared__ double redd[8];
     const int ldp1 = p1_ld(k);
     const int kq = ldp1 / 4;
-    const int row0 = blockIdx.x * kUpdRows;
-    const int rows = min(kUpdRows, n - row0);
+    const int i = blockIdx.x * kUpdRows + (int)threadIdx.x / kq;
+    const int c = 4 * ((int)threadIdx.x % kq);
     double acc = 0.0;
-    for (int e = threadIdx.x; e < rows * kq; e += 256) {
-        const int i = row0 + e / kq;
-        const int c = 4 * (e % kq);
+    if (i < n) {
         const int si = i / kSymStrip;
         floatx4 sum = {0.f, 0.f, 0.f, 0.f};
         int sp = si;
-        for (; sp + 8 <= NS; sp += 8) {
-            floatx4 v[8];
+        for (; sp + kFoldInFlight <= NS; sp += kFoldInFlight) {
+            floatx4 v[kFoldInFlight];
 #pragma unroll
-            for (int u = 0; u < 8; ++u)
+            for (int u = 0; u < kFoldInFlight; ++u)
                 v[u] = *reinterpret_cast<const floatx4*>(P1 + (p1_rows_before(sp + u) + i) * ldp1 + c);
 #pragma unroll
-            for (int u = 0; u < 8; ++u) sum += v[u];
+            for (int u = 0; u < kFoldInFlight; ++u) sum += v[u];
         }
         for (; sp < NS; ++sp)
             sum += *reinterpret_cast<const floatx4*>(P1 + (p1_rows_before(sp) + i) * ldp1 + c);
         const int nch = (min(n, kSymStrip * (si + 1)) + kSymChunk - 1) / kSymChunk;
         const int64_t qstride = (int64_t)NS * kSymStrip * ldp1;
         const float* p2 = P2 + ((int64_t)si * kSymStrip + (i - si * kSymStrip)) * ldp1 + c;
-        for (int q = 0; q < nch; ++q) sum += *reinterpret_cast<const floatx4*>(p2 + q * qstride);
+        int q = 0;
+        for (; q + 8 <= nch; q += 8) {
+            floatx4 v[8];
+#pragma unroll
+            for (int u = 0; u < 8; ++u)
+                v[u] = *reinterpret_cast<const floatx4*>(p2 + (q + u) * qstride);
+#pragma unroll
+            for (int u = 0; u < 8; ++u) sum += v[u];
+        }
+        for (; q < nch; ++q) sum += *reinterpret_cast<const floatx4*>(p2 + q * qstride);
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
             if (c + j < k) {
@@ -476,8 +488,16 @@ __global__ __launch_bounds__(256) void sym_fold_kernel(const float* __restrict__
         }
     }
     if (tr_part) {
-        const double t = block_sum256(acc, redd);
-        if (threadIdx.x == 0) tr_part[blockIdx.x] = t;
+        // the block's waves in order (blockDim is a multiple of 64)
+        acc = wave_sum(acc);
+        const int w = threadIdx.x >> 6;
+        if ((threadIdx.x & 63) == 0) redd[w] = acc;
+        __syncthreads();
+        if (threadIdx.x == 0) {
+            double t = 0.0;
+            for (int v = 0; v < (int)(blockDim.x >> 6); ++v) t += redd[v];
+            tr_part[blockIdx.x] = t;
+        }
     }
 }
 
@@ -535,8 +555,9 @@ hipError_t launch_sym_fold(const float* P1, const float* P2, int n, int k, const
                            float* P, int ldP, const float* Hdot, double* tr_part,
                            const int* done, hipStream_t st) {
     const int nblk = (n + kUpdRows - 1) / kUpdRows;
-    hipLaunchKernelGGL(sym_fold_kernel, dim3(nblk), dim3(256), 0, st, P1, P2, n, k, p.ns, P, ldP,
-                       Hdot, tr_part, done);
+    const int threads = kUpdRows * (p1_ld(k) / 4);  // one per row and four factors
+    hipLaunchKernelGGL(sym_fold_kernel, dim3(nblk), dim3(threads), 0, st, P1, P2, n, k, p.ns, P,
+                       ldP, Hdot, tr_part, done);
     return hipGetLastError();
 }
 
