@@ -43,9 +43,12 @@ def _check(P, tr, S64, H64, rel=REL):
 
 # n: one block, ragged blocks, one strip (512) and its edges, several strips,
 # several 4096-row chunks (4097, 9000) with a ragged tail; k: one and two
-# 16-column tiles, full and partial
+# 16-column tiles, full and partial. A last tile with at most 8 factors runs as
+# a half tile (two parts of H per operand: k = 1, 8, 17, 20, 24); one with more
+# runs as a full tile with zero factors (k = 13, 28) or none (k = 16, 32).
 SYM_CASES = [(1, 1), (5, 8), (32, 16), (33, 24), (100, 17), (511, 24), (512, 32), (513, 24),
-             (1000, 8), (1537, 24), (4097, 24), (5000, 32), (9000, 24), (2048, 1), (3001, 20)]
+             (1000, 8), (1537, 24), (4097, 24), (5000, 32), (9000, 24), (2048, 1), (3001, 20),
+             (777, 13), (2050, 28)]
 
 
 @pytest.mark.parametrize("n,k", SYM_CASES)
