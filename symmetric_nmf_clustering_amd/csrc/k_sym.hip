@@ -384,7 +384,11 @@ __global__ __launch_bounds__(64 * kSymWaves) void sym_kernel(
     };
 
     // One panel: issue the next panel's packed H rows and S, multiply this
-    // one, stage the next H block, one barrier, then the row-side reduction.
+    // one, reduce the previous panel's row sums, stage the next H block, one
+    // barrier. The reduction of panel a - 1 reads the red buffer its waves
+    // wrote before the last barrier, and panel a + 1 writes that buffer only
+    // after the coming one; reducing it here rather than right after the
+    // barrier lets the next loads go out as soon as the barrier is passed.
     // Loads are issued on every path (clamped to the chunk's last panel), so
     // the compiler's wait counts stay tight; past the chunk's end only the
     // arithmetic is skipped.
@@ -393,9 +397,9 @@ __global__ __launch_bounds__(64 * kSymWaves) void sym_kernel(
         load_h(an);  // first: waiting for it before the barrier leaves the S loads in flight
         load(an, nxt);
         if (a < a1) compute(a, cur);
+        if (a > a0 && a - 1 < a1) reduce_rows(a - 1);
         store_h((a + 1) & 1);  // that buffer was last read before the previous barrier
         __syncthreads();
-        if (a < a1) reduce_rows(a);
     };
 
     Panel va, vb;
@@ -407,6 +411,8 @@ __global__ __launch_bounds__(64 * kSymWaves) void sym_kernel(
         panel(a, va, vb);
         panel(a + 1, vb, va);
     }
+    // an even panel count ends on a computed panel whose sums no call reduced
+    if ((a1 - a0) % 2 == 0) reduce_rows(a1 - 1);
 
     // column side of the chunk: lane (lr, g') holds column c0 + 4 lr + q,
     // factors 16t + 4g' + r (a half tile's rows 8..15 folded into 0..7 first)
