@@ -69,7 +69,7 @@ enum symnmf_solver { SYMNMF_AUTO = 0, SYMNMF_FULL = 1, SYMNMF_BLOCK_SVRG = 2 };
  * (symnmf_sh_sym; P1 "Factorization at scale"; S = S^T since P1's introduction
  * defines S as an absolute correlation or a TPDM, both symmetric): half
  * the bytes of S per step, for k <= 32, with a workspace larger by about
- * k n^2 / 256 bytes. The Block-SVRG sampled steps read row panels either way. */
+ * 3 k n^2 / 512 bytes. The Block-SVRG sampled steps read row panels either way. */
 enum symnmf_sh_pass { SYMNMF_SH_ROWS = 0, SYMNMF_SH_UPPER = 1 };
 
 /* Initialisation of H (P1 "Factorizing with SymNMF": the same fixed-seed

@@ -38,8 +38,8 @@
 //    the same factors as rows 0..7 (tile_mma): four matrix-core steps per K
 //    block instead of six. The two halves of the result are added at the end.
 //
-// Work: strips of 512 columns (8 waves), each walked down in chunks of 4096
-// rows. Workgroup (strip s, chunk qc) covers rows [4096 qc, min(4096 (qc+1),
+// Work: strips of 512 columns (8 waves), each walked down in chunks of 2048
+// rows. Workgroup (strip s, chunk qc) covers rows [2048 qc, min(2048 (qc+1),
 // E_s)), E_s = min(n, 512 (s + 1)): the part of the strip on or above the
 // diagonal. Per 32-row panel the eight waves' row-side sums meet in LDS and
 // leave as one partial P1[s][i] per (strip, row; rows of p1_ld(k) floats);
@@ -441,7 +441,7 @@ __global__ __launch_bounds__(64 * kSymWaves) void sym_kernel(
 // four factors (blockDim = kUpdRows * p1_ld(k) / 4: float4 loads of the
 // p1_ld(k)-float rows of P1 and P2), each summed in the same order as a scalar
 // sum would. A row adds up to ns strip partials (rows near the top the most)
-// and up to n / 4096 chunk partials (rows near the bottom): kFoldInFlight and
+// and up to n / 2048 chunk partials (rows near the bottom): kFoldInFlight and
 // 8 loads are issued before their additions, so neither sum waits for a
 // memory round trip per partial.
 constexpr int kFoldInFlight = 16;

@@ -87,11 +87,11 @@ hipError_t launch_sq_split(const float* S, int64_t lds, const void* Qs, int n, i
 // packed twice (launch_sym_pack: the column side's and the row side's K maps).
 // The pass writes row-side partials P1 (one per 512-column strip and row,
 // compact: strip s holds rows [0, min(n, 512 (s + 1)))) and column-side
-// partials P2 (one per 4096-row chunk, strip and column of the strip); the
+// partials P2 (one per 2048-row chunk, strip and column of the strip); the
 // fold adds them in a fixed order into P (n x k, ld ldP), with the trace
 // partials as launch_reduce_partials (Hdot n x k, ld k).
 constexpr int kSymStrip = 512;   // columns per strip
-constexpr int kSymChunk = 4096;  // rows per chunk
+constexpr int kSymChunk = 2048;  // rows per chunk
 constexpr int kSymMaxK = 32;     // widest factor of the symmetric pass
 struct SymPlan {
     int nt;                   // 16-column tiles of H

@@ -211,11 +211,11 @@ def test_fullsize_tpdm_rows_trace_and_spectrum(big):
 
 def test_fullsize_sh_sym_rows(big):
     """The upper-triangle pass as the benchmark's fit runs it (k = 24, 512-column
-    strips, 4096-row chunks): sampled rows, strip and chunk edges among them,
+    strips, 2048-row chunks): sampled rows, strip and chunk edges among them,
     against the oracle's rows built from the returns; the trace against the sum
     of its own outputs; and the row-panel pass on the same rows."""
     torch, api, w, S, fro, rows = big
-    rows = np.unique(np.concatenate([rows, [4096, 8191, 8192, 99839, 99840]]))
+    rows = np.unique(np.concatenate([rows, [2047, 2048, 4095, 4096, 8191, 8192, 99839, 99840]]))
     H = synth.random_factor(N, K, seed=3, scale=0.1)
     Hd = to_dev(H, torch)
     P, tr = api.sh_sym(S, Hd)

@@ -42,7 +42,7 @@ def _check(P, tr, S64, H64, rel=REL):
 
 
 # n: one block, ragged blocks, one strip (512) and its edges, several strips,
-# several 4096-row chunks (4097, 9000) with a ragged tail; k: one and two
+# several 2048-row chunks (2049, 4097, 5000, 9000) with a ragged tail; k: one and two
 # 16-column tiles, full and partial. A last tile with at most 8 factors runs as
 # a half tile (two parts of H per operand: k = 1, 8, 17, 20, 24); one with more
 # runs as a full tile with zero factors (k = 13, 28) or none (k = 16, 32).
