@@ -216,8 +216,10 @@ __global__ __launch_bounds__(64 * kSymWaves) void sym_kernel(
 
     typedef floatx4 Panel[8];
     auto load = [&](int a, Panel& v) {
-        const int64_t row0 = 32 * (int64_t)a;
-        const int64_t rest = ((int64_t)n - row0) * lds * 4;  // bytes from the panel to S's end
+        const int64_t row0 = 32 * (int64_t)min(a, a1 - 1);
+        // bytes from the panel to S's end; a panel past the chunk gets an empty
+        // buffer, whose loads return zeros without a memory access
+        const int64_t rest = a < a1 ? ((int64_t)n - row0) * lds * 4 : 0;
         const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
             (void*)(S + row0 * lds), (short)0, (int)min(rest, (int64_t)0x7fffffff), 0x00020000);
 #pragma unroll
@@ -389,13 +391,14 @@ __global__ __launch_bounds__(64 * kSymWaves) void sym_kernel(
     // wrote before the last barrier, and panel a + 1 writes that buffer only
     // after the coming one; reducing it here rather than right after the
     // barrier lets the next loads go out as soon as the barrier is passed.
-    // Loads are issued on every path (clamped to the chunk's last panel), so
-    // the compiler's wait counts stay tight; past the chunk's end only the
-    // arithmetic is skipped.
+    // Loads are issued on every path, so the compiler's wait counts stay
+    // tight: the S loads of a panel past the chunk's end read an empty buffer
+    // (zeros, no memory access) and the H loads are clamped to the last block;
+    // past the chunk's end only the arithmetic is skipped.
     auto panel = [&](int a, Panel& cur, Panel& nxt) {
         const int an = min(a + 1, a1 - 1);
         load_h(an);  // first: waiting for it before the barrier leaves the S loads in flight
-        load(an, nxt);
+        load(a + 1, nxt);
         if (a < a1) compute(a, cur);
         if (a > a0 && a - 1 < a1) reduce_rows(a - 1);
         store_h((a + 1) & 1);  // that buffer was last read before the previous barrier
