@@ -45,10 +45,11 @@ def _check(P, tr, S64, H64, rel=REL):
 # several 2048-row chunks (2049, 4097, 5000, 9000) with a ragged tail; k: one and two
 # 16-column tiles, full and partial. A last tile with at most 8 factors runs as
 # a half tile (two parts of H per operand: k = 1, 8, 17, 20, 24); one with more
-# runs as a full tile with zero factors (k = 13, 28) or none (k = 16, 32).
+# runs as a full tile with zero factors (k = 9, 13, 28, 31) or none (k = 16, 32).
+# n = 2048 and 6144 end exactly on a chunk edge, 6145 one row past it.
 SYM_CASES = [(1, 1), (5, 8), (32, 16), (33, 24), (100, 17), (511, 24), (512, 32), (513, 24),
              (1000, 8), (1537, 24), (4097, 24), (5000, 32), (9000, 24), (2048, 1), (3001, 20),
-             (777, 13), (2050, 28)]
+             (777, 13), (2050, 28), (2048, 24), (6144, 31), (6145, 9)]
 
 
 @pytest.mark.parametrize("n,k", SYM_CASES)
